@@ -1,0 +1,142 @@
+// gdn_common.h -- device-side building blocks shared by the GDN prefill
+// kernels (gfx950 / CDNA4, wave64).
+//
+// Matrix products use the CDNA matrix cores:
+//   bf16: v_mfma_f32_16x16x32_bf16  (A 16x32, B 32x16, C 16x16 fp32)
+//   fp32: v_mfma_f32_16x16x4_f32    (A 16x4,  B 4x16,  C 16x16 fp32)
+// Lane l = 16*g + c (g = l / 16 in 0..3, c = l % 16).  With KPL contraction
+// elements per lane per instruction (8 for bf16, 1 for fp32):
+//   A operand: lane holds A[c][KPL*g + e], e < KPL   (row c of the 16-row tile)
+//   B operand: lane holds B[KPL*g + e][c]            (column c)
+//   C result : lane holds C[4*g + r][c], r < 4
+//
+// Register reuse across a chain of products.  A 16-row result tile leaves
+// rows 4g..4g+3 in lane group g.  If the next product contracts over those
+// rows, visiting them in the order
+//     pi(g, s) = 16*(s / 4) + 4*g + (s % 4)         (slot s of lane group g)
+// makes the result registers, taken in slot order, exactly the next B
+// operand (slot s = KPL*kt + e for k-step kt, element e).  The other operand
+// must then be stored with its contraction index permuted by pi.  The
+// workspace therefore holds operands "fragment-major": for a 16-row tile and
+// k-step kt, the 64 lanes' KPL-element fragments are contiguous, so every
+// operand load is one coalesced 64*KPL-element block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kChunk = 64;
+constexpr float kNormEps = 1e-6f;
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
+
+// Matrix-core traits per compute type.
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16> {
+  static constexpr int KPL = 8;
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void set(frag &f, int e, float x) { f[e] = (bf16)x; }
+  static __device__ __forceinline__ float get(const frag &f, int e) { return (float)f[e]; }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int KPL = 1;
+  typedef float frag;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void set(frag &f, int, float x) { f = x; }
+  static __device__ __forceinline__ float get(const frag &f, int) { return f; }
+};
+
+// Contraction index of slot s in lane group g (see the header comment).
+__device__ __forceinline__ int pi_idx(int g, int s) {
+  return 16 * (s >> 2) + 4 * g + (s & 3);
+}
+
+// ---------------------------------------------------------------------------
+// Workspace geometry.  Everything per (flat chunk f, sab head h); ch = f*H + h.
+//   Wf : [ch][4 row tiles][D/(4K) ksteps][64][K]      W, contraction dk in pi order
+//   Kf : [ch][D/16 row tiles][64/(4K)][64][K]          Ktilde^T, contraction t in pi order
+//   Uf : [ch][D/16 dv tiles][4 row tiles][64][4]       U in result layout
+//   Gw : [ch][64] fp32                                 cumulative log gate
+//   Hf : [ch][D/16 dv tiles][D/(4K)][64][K]            chunk-start state, dk in pi order
+//   Nf : [ch][D/16 dv tiles][64/(4K)][64][K]           new values, t in pi order
+// (K = KPL.)  Each block is 64*D elements except Gw (64) and Hf (D*D).
+// ---------------------------------------------------------------------------
+template <typename T, int D> struct Geo {
+  static constexpr int KPL = Mfma<T>::KPL;
+  static constexpr int NT = D / 16;             // 16-wide tiles along D
+  static constexpr int KS_D = D / (4 * KPL);     // k-steps contracting over D
+  static constexpr int KS_C = kChunk / (4 * KPL);// k-steps contracting over a chunk
+  static constexpr int64_t W_ELEMS = 64 * D;
+  static constexpr int64_t H_ELEMS = (int64_t)D * D;
+};
+
+// ---------------------------------------------------------------------------
+// Canonical row L2 normalisation.  Four cooperating lanes (lane ^ 1, lane ^ 2
+// partners, i.e. lanes 4r..4r+3) share one row of D elements; lane part p owns
+// the 8-element runs x with (x / 8) % 4 == p.  Sum of squares in fp32 in
+// increasing x within a lane, then (p0 + p1) + (p2 + p3).  Every kernel that
+// normalises q or k uses this, so all of them see bit-identical rows.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ float row_inv_norm(const float (&x)[D / 4]) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 4; ++i) s = fmaf(x[i], x[i], s);
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  return 1.0f / sqrtf(s + kNormEps);
+}
+
+// Element index (within a row of D) of the i-th value owned by lane part p.
+__device__ __forceinline__ int row_part_idx(int p, int i) {
+  return 32 * (i >> 3) + 8 * p + (i & 7);
+}
+
+// Load a token row part for row-normalisation, as fp32.
+template <typename Tin, int D>
+__device__ __forceinline__ void load_row_part(const Tin *row, int p, float (&x)[D / 4]) {
+#pragma unroll
+  for (int i = 0; i < D / 4; i += 8) {
+    const Tin *src = row + 32 * (i >> 3) + 8 * p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[i + e] = to_f32(src[e]);
+  }
+}
+
+// fp32 exp of a (non-positive) log-gate difference.
+__device__ __forceinline__ float gexp(float x) { return __expf(x); }
+
+// Generic state element access for the three state dtypes.
+__device__ __forceinline__ float load_state_elem(const void *base, int dtype, int64_t off) {
+  if (dtype == 0) return ((const float *)base)[off];
+  if (dtype == 1) return (float)((const bf16 *)base)[off];
+  return (float)((const _Float16 *)base)[off];
+}
+__device__ __forceinline__ void store_state_elem(void *base, int dtype, int64_t off, float x) {
+  if (dtype == 0) ((float *)base)[off] = x;
+  else if (dtype == 1) ((bf16 *)base)[off] = (bf16)x;
+  else ((_Float16 *)base)[off] = (_Float16)x;
+}
+
+}  // namespace gdn

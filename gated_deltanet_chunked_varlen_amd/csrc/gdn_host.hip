@@ -1,0 +1,293 @@
+// gdn_host.hip -- the C ABI of libgdn_prefill: host-side checks, workspace
+// planning and the launch sequence.
+//
+// Argument rules follow gitcode "FlashInfer GDN Prefill 完全指南" (sections
+// "API 全参数解析", "状态池", "中间状态检查点", "约束与注意点"): head sharing
+// (hq == hk and hv % hq == 0) or (hk == hv and hq % hk == 0); checkpoint
+// interval a multiple of 64 with its two buffers given together; an output
+// pool required with state_indices and a final state; max_seqlen within
+// [ceil(T/N), T].  Nothing here reads device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/gdn_prefill.h"
+#include "gdn_internal.h"
+
+using namespace gdn;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int32_t sab_heads(const gdn_prefill_params *p) {
+  return std::max(p->num_q_heads, p->num_v_heads);
+}
+
+size_t elem_size(int dtype) { return dtype == GDN_F32 ? 4 : 2; }
+
+bool valid_state_dtype(int d) { return d == GDN_F32 || d == GDN_BF16 || d == GDN_F16; }
+bool valid_itype(int t) { return t == GDN_I32 || t == GDN_I64; }
+
+struct Layout {
+  size_t chunk_idx, cu_chunks, seq_bos, n_chunks, Wf, Kf, Uf, Hf, Nf, Gw, total;
+};
+
+Layout plan(const gdn_prefill_params *p) {
+  Layout L{};
+  const int64_t cap = gdn_max_chunks(p->total_tokens, p->num_seqs);
+  const int64_t H = sab_heads(p), D = p->head_size, N = p->num_seqs;
+  const size_t es = elem_size(p->qkv_dtype);
+  const size_t blocks = (size_t)cap * (size_t)H;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  L.chunk_idx = take(sizeof(int32_t) * 2 * (size_t)std::max<int64_t>(cap, 1));
+  L.cu_chunks = take(sizeof(int32_t) * (size_t)(N + 1));
+  L.seq_bos = take(sizeof(int32_t) * (size_t)(N + 1));
+  L.n_chunks = take(sizeof(int32_t));
+  L.Wf = take(blocks * 64 * D * es);
+  L.Kf = take(blocks * 64 * D * es);
+  L.Uf = take(blocks * 64 * D * es);
+  L.Nf = take(blocks * 64 * D * es);
+  L.Hf = take(blocks * D * D * es);
+  L.Gw = take(blocks * 64 * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+bool strides_ok(const int64_t s[4], int64_t rows, int64_t H, int64_t D) {
+  if (s[0] == 0 && s[1] == 0 && s[2] == 0 && s[3] == 0) return true;
+  int64_t ext[4] = {rows, H, D, D};
+  int idx[4] = {0, 1, 2, 3};
+  for (int i = 0; i < 4; ++i)
+    if (s[i] <= 0) return false;
+  std::sort(idx, idx + 4, [&](int x, int y) { return s[x] < s[y]; });
+  for (int k = 0; k + 1 < 4; ++k) {
+    // a dimension of extent 1 never overlaps anything
+    if (ext[idx[k]] <= 1) continue;
+    if (s[idx[k + 1]] < s[idx[k]] * ext[idx[k]]) return false;
+  }
+  return true;
+}
+
+void fill_strides(const int64_t in[4], int64_t H, int64_t D, int64_t out[4]) {
+  if (in[0] == 0 && in[1] == 0 && in[2] == 0 && in[3] == 0) {
+    out[3] = 1;
+    out[2] = D;
+    out[1] = D * D;
+    out[0] = H * D * D;
+  } else {
+    for (int i = 0; i < 4; ++i) out[i] = in[i];
+  }
+}
+
+int check_device() {
+  static std::mutex mu;
+  static int cached[64];
+  static bool init = false;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GDN_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!init) {
+    for (int i = 0; i < 64; ++i) cached[i] = 0;
+    init = true;
+  }
+  if (dev < 0 || dev >= 64) return GDN_ERR_DEVICE;
+  if (cached[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GDN_ERR_DEVICE;
+    cached[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  return cached[dev] == 1 ? GDN_OK : GDN_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char *gdn_status_string(int code) {
+  switch (code) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "invalid token, sequence or head counts, or head size not in {32, 64, 128}";
+    case GDN_ERR_HEAD_RATIO: return "illegal head sharing: need (hq == hk and hv % hq == 0) or (hk == hv and hq % hk == 0)";
+    case GDN_ERR_DTYPE: return "unsupported dtype or index type";
+    case GDN_ERR_CHECKPOINT: return "checkpoint_every_n_tokens must be a non-negative multiple of 64 and state_checkpoints / checkpoint_cu_starts must be given together";
+    case GDN_ERR_STATE: return "inconsistent state arguments (output_state required for a final state; pool_size required with state_indices)";
+    case GDN_ERR_MAX_SEQLEN: return "max_seqlen outside [ceil(total_tokens / num_seqs), total_tokens]";
+    case GDN_ERR_WORKSPACE: return "workspace missing or smaller than gdn_prefill_workspace_size()";
+    case GDN_ERR_STRIDES: return "state strides must be all zero (contiguous) or positive and non-overlapping";
+    case GDN_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
+    case GDN_ERR_LAUNCH: return "kernel launch failed";
+    case (int)GDN_STATUS_CU_SEQLENS: return "status: cu_seqlens not non-decreasing within [0, total_tokens]";
+    case (int)GDN_STATUS_CHECKPOINT_STARTS: return "status: checkpoint_cu_starts differs from the prefix sum of floor(len / n)";
+    case (int)GDN_STATUS_STATE_INDEX: return "status: a state index is outside [0, pool_size)";
+    case (int)GDN_STATUS_CHUNK_CAPACITY: return "status: chunk table capacity exceeded";
+    default: return "unknown code";
+  }
+}
+
+int64_t gdn_max_chunks(int64_t total_tokens, int32_t num_seqs) {
+  if (total_tokens <= 0 || num_seqs <= 0) return 0;
+  const int64_t m = std::min<int64_t>(num_seqs, total_tokens);
+  return (total_tokens + 63 * m) / 64;
+}
+
+static int check_shape(const gdn_prefill_params *p) {
+  if (!p) return GDN_ERR_NULL;
+  if (p->total_tokens < 0 || p->total_tokens > INT32_MAX - 64 || p->num_seqs < 0) return GDN_ERR_SHAPE;
+  if (p->num_q_heads < 1 || p->num_k_heads < 1 || p->num_v_heads < 1) return GDN_ERR_SHAPE;
+  if (p->head_size != 32 && p->head_size != 64 && p->head_size != 128) return GDN_ERR_SHAPE;
+  if (!p->cu_seqlens && p->num_seqs != 1) return GDN_ERR_SHAPE;
+  const int32_t hq = p->num_q_heads, hk = p->num_k_heads, hv = p->num_v_heads;
+  const bool gva = (hq == hk) && (hv % hq == 0);
+  const bool gqa = (hk == hv) && (hq % hk == 0);
+  if (!gva && !gqa) return GDN_ERR_HEAD_RATIO;
+  if (p->qkv_dtype != GDN_F32 && p->qkv_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+  return GDN_OK;
+}
+
+size_t gdn_prefill_workspace_size(const gdn_prefill_params *p) {
+  if (check_shape(p) != GDN_OK) return 0;
+  return plan(p).total;
+}
+
+int gdn_validate_host(const gdn_prefill_params *p) {
+  int rc = check_shape(p);
+  if (rc != GDN_OK) return rc;
+  const int64_t T = p->total_tokens, N = p->num_seqs, H = sab_heads(p), D = p->head_size;
+  if (T > 0 && (!p->q || !p->k || !p->v || !p->output)) return GDN_ERR_NULL;
+  if (p->cu_seqlens && !valid_itype(p->cu_seqlens_type)) return GDN_ERR_DTYPE;
+  // states
+  if (p->initial_state && !valid_state_dtype(p->initial_state_dtype)) return GDN_ERR_DTYPE;
+  if (p->output_final_state) {
+    if (!p->output_state) return GDN_ERR_STATE;
+    if (!valid_state_dtype(p->output_state_dtype)) return GDN_ERR_DTYPE;
+  }
+  int64_t rows = N;
+  if (p->state_indices) {
+    if (!valid_itype(p->state_indices_type)) return GDN_ERR_DTYPE;
+    if (p->pool_size < 1) return GDN_ERR_STATE;
+    rows = p->pool_size;
+  }
+  if (p->initial_state && !strides_ok(p->initial_state_strides, rows, H, D)) return GDN_ERR_STRIDES;
+  if (p->output_final_state && !strides_ok(p->output_state_strides, rows, H, D)) return GDN_ERR_STRIDES;
+  // checkpoints
+  if (p->checkpoint_every_n_tokens < 0) return GDN_ERR_CHECKPOINT;
+  if ((p->state_checkpoints == nullptr) != (p->checkpoint_cu_starts == nullptr)) return GDN_ERR_CHECKPOINT;
+  if (p->checkpoint_every_n_tokens > 0) {
+    if (p->checkpoint_every_n_tokens % GDN_CHUNK != 0) return GDN_ERR_CHECKPOINT;
+    if (!p->state_checkpoints) return GDN_ERR_CHECKPOINT;
+    if (!valid_state_dtype(p->checkpoint_dtype)) return GDN_ERR_DTYPE;
+    if (!valid_itype(p->checkpoint_cu_starts_type)) return GDN_ERR_DTYPE;
+    if (p->checkpoint_rows < 0) return GDN_ERR_CHECKPOINT;
+  }
+  // max_seqlen
+  if (p->max_seqlen < 0) return GDN_ERR_MAX_SEQLEN;
+  if (p->max_seqlen > 0 && N > 0) {
+    const int64_t lo = (T + N - 1) / N;
+    if (p->max_seqlen < lo || p->max_seqlen > T) return GDN_ERR_MAX_SEQLEN;
+  }
+  // workspace
+  const size_t need = plan(p).total;
+  if (p->workspace_bytes < need || (need > 0 && !p->workspace)) return GDN_ERR_WORKSPACE;
+  return GDN_OK;
+}
+
+int gdn_build_chunk_indices(const void *cu_seqlens, int32_t cu_type, int32_t num_seqs,
+                            int64_t total_tokens, int32_t *chunk_indices, int32_t *cu_chunks,
+                            int32_t *seq_starts, int32_t *n_chunks, int32_t *status,
+                            void *stream) {
+  if (num_seqs < 0 || total_tokens < 0 || total_tokens > INT32_MAX - 64) return GDN_ERR_SHAPE;
+  if (!cu_seqlens && num_seqs != 1) return GDN_ERR_SHAPE;
+  if (cu_seqlens && !valid_itype(cu_type)) return GDN_ERR_DTYPE;
+  const int64_t cap = gdn_max_chunks(total_tokens, num_seqs);
+  if (!cu_chunks || !seq_starts || !n_chunks || (cap > 0 && !chunk_indices)) return GDN_ERR_NULL;
+  int rc = check_device();
+  if (rc != GDN_OK) return rc;
+  hipError_t e = launch_chunk_index(cu_seqlens, cu_type, num_seqs, total_tokens, cap,
+                                    chunk_indices, cu_chunks, seq_starts, n_chunks, status,
+                                    nullptr, 0, 0, nullptr, 0, 0, (hipStream_t)stream);
+  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+int gdn_prefill(const gdn_prefill_params *p, void *stream) {
+  int rc = gdn_validate_host(p);
+  if (rc != GDN_OK) return rc;
+  rc = check_device();
+  if (rc != GDN_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const Layout L = plan(p);
+  unsigned char *ws = (unsigned char *)p->workspace;
+  const int64_t H = sab_heads(p), D = p->head_size;
+
+  Args a;
+  std::memset(&a, 0, sizeof(a));
+  a.T = p->total_tokens;
+  a.N = p->num_seqs;
+  a.H = (int32_t)H;
+  a.hq = p->num_q_heads;
+  a.hk = p->num_k_heads;
+  a.hv = p->num_v_heads;
+  a.D = (int32_t)D;
+  a.dtype = p->qkv_dtype;
+  a.q = p->q;
+  a.k = p->k;
+  a.v = p->v;
+  a.g = p->g;
+  a.beta = p->beta;
+  a.scale = p->has_scale ? p->scale : (float)(1.0 / std::sqrt((double)D));
+  a.l2norm = p->use_qk_l2norm_in_kernel ? 1 : 0;
+  a.out = p->output;
+  a.chunk_idx = (int32_t *)(ws + L.chunk_idx);
+  a.cu_chunks = (int32_t *)(ws + L.cu_chunks);
+  a.seq_bos = (int32_t *)(ws + L.seq_bos);
+  a.n_chunks = (int32_t *)(ws + L.n_chunks);
+  a.cap = gdn_max_chunks(p->total_tokens, p->num_seqs);
+  a.Wf = ws + L.Wf;
+  a.Kf = ws + L.Kf;
+  a.Uf = ws + L.Uf;
+  a.Hf = ws + L.Hf;
+  a.Nf = ws + L.Nf;
+  a.Gw = (float *)(ws + L.Gw);
+  const int64_t rows = p->state_indices ? p->pool_size : p->num_seqs;
+  a.init = p->initial_state;
+  a.init_dtype = p->initial_state_dtype;
+  fill_strides(p->initial_state_strides, H, D, a.init_str);
+  a.init_rows = rows;
+  a.outst = p->output_state;
+  a.out_dtype = p->output_state_dtype;
+  fill_strides(p->output_state_strides, H, D, a.out_str);
+  a.out_final = p->output_final_state ? 1 : 0;
+  a.sidx = p->state_indices;
+  a.sidx_type = p->state_indices_type;
+  a.pool_rows = rows;
+  a.ck_every = p->checkpoint_every_n_tokens;
+  a.ck = p->state_checkpoints;
+  a.ck_dtype = p->checkpoint_dtype;
+  const int64_t zero4[4] = {0, 0, 0, 0};
+  fill_strides(zero4, H, D, a.ck_str);
+  a.ck_rows = p->checkpoint_rows;
+  a.ck_cs = p->checkpoint_cu_starts;
+  a.ck_cs_type = p->checkpoint_cu_starts_type;
+  a.status = p->status;
+  if (a.ck_every > 0 && !a.ck) a.ck_every = 0;
+
+  hipError_t e = launch_chunk_index(p->cu_seqlens, p->cu_seqlens_type, a.N, a.T, a.cap,
+                                    a.chunk_idx, a.cu_chunks, a.seq_bos, a.n_chunks, a.status,
+                                    a.ck_every > 0 ? a.ck_cs : nullptr, a.ck_cs_type, a.ck_every,
+                                    a.sidx, a.sidx_type, a.pool_rows, s);
+  if (e == hipSuccess && a.cap > 0) e = launch_intra(a, s);
+  if (e == hipSuccess) e = launch_state(a, s);
+  if (e == hipSuccess && a.cap > 0) e = launch_output(a, s);
+  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,167 @@
+// k3_output.hip -- output pass.
+//
+// Every token reads the state after its own update (weigao.cc "GDN 与 Chunked
+// Prefill", section "块内 state 和块间 final state").  Inside a chunk that
+// starts from state S with new values N (0539edu "GDN与线性注意力GPU并行实现",
+// section 3.3: one product for what the chunk reads from its start state, one
+// triangular-masked product for what it wrote itself):
+//
+//   O = scale * ( diag(exp(G)) Q S + (Q K^T .* M) N ),
+//   M[t][j] = exp(G_t - G_j) for j <= t, else 0.
+//
+// One workgroup of four wave64s per (flat chunk, sab head); wave w produces
+// output rows 16w..16w+15 for all value columns.  q and k rows are staged in
+// LDS (normalised when asked, with the same row normalisation as the
+// intra-chunk pass).  P^T = K Q^T is formed so that each lane ends up holding
+// rows of P in the order the next product contracts over (pi order), matching
+// the stored N.  Rows beyond the sequence end are not stored.
+#include "gdn_common.h"
+#include "gdn_internal.h"
+#include "../../include/gdn_prefill.h"
+
+namespace gdn {
+
+template <typename T, int D>
+struct OutSmem {
+  T Qs[64][D + 16 / sizeof(T)];
+  T Ks[64][D + 16 / sizeof(T)];
+  float Gs[64];
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) output_kernel(Args a) {
+  using M = Mfma<T>;
+  using Ge = Geo<T, D>;
+  typedef typename M::frag frag;
+  constexpr int KPL = Ge::KPL, NT = Ge::NT, KS_D = Ge::KS_D, KS_C = Ge::KS_C;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  OutSmem<T, D> &sm = *reinterpret_cast<OutSmem<T, D> *>(smem_raw);
+
+  const int64_t ch = blockIdx.x;
+  const int H = a.H;
+  const int f = (int)(ch / H), h = (int)(ch % H);
+  if (f >= a.n_chunks[0]) return;
+  const int seq = a.chunk_idx[2 * f], cidx = a.chunk_idx[2 * f + 1];
+  const int64_t bos = (int64_t)a.seq_bos[seq] + (int64_t)kChunk * cidx;
+  const int len = (int)min<int64_t>(kChunk, (int64_t)a.seq_bos[seq + 1] - bos);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+
+  {
+    const int t = tid >> 2, p = tid & 3;
+    const bool valid = t < len;
+    const int qh = h / (H / a.hq), kh = h / (H / a.hk);
+    float x[D / 4];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (valid) {
+        const T *row = pass == 0 ? (const T *)a.q + ((bos + t) * a.hq + qh) * D
+                                 : (const T *)a.k + ((bos + t) * a.hk + kh) * D;
+        load_row_part<T, D>(row, p, x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < D / 4; ++e) x[e] = 0.f;
+      }
+      float inv = 1.f;
+      if (a.l2norm) inv = row_inv_norm<D>(x);
+      T(*dst)[D + 16 / sizeof(T)] = pass == 0 ? sm.Qs : sm.Ks;
+#pragma unroll
+      for (int e = 0; e < D / 4; ++e) dst[t][row_part_idx(p, e)] = from_f32<T>(x[e] * inv);
+    }
+    if (tid < 64) sm.Gs[tid] = a.Gw[ch * kChunk + tid];
+  }
+  __syncthreads();
+
+  const int tt = wave;
+  // P rows of this tile as operand fragments over j in pi order
+  frag pf[KS_C];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (jt <= tt) {
+#pragma unroll
+      for (int kt = 0; kt < KS_D; ++kt) {
+        const int k0 = kt * 4 * KPL + g * KPL;
+        const frag fa = *reinterpret_cast<const frag *>(&sm.Ks[16 * jt + c][k0]);
+        const frag fb = *reinterpret_cast<const frag *>(&sm.Qs[16 * tt + c][k0]);
+        acc = M::mma(fa, fb, acc);
+      }
+    }
+    // acc[r] = P[t = 16tt + c][j = 16jt + 4g + r]
+    const int t = 16 * tt + c;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * jt + 4 * g + r;
+      const float pv = (j <= t) ? acc[r] * gexp(sm.Gs[t] - sm.Gs[j]) : 0.f;
+      const int s = 4 * jt + r;
+      M::set(pf[s / KPL], s % KPL, pv);
+    }
+  }
+  // Q fragments for Q S (contraction over dk in pi order)
+  frag qf[KS_D];
+#pragma unroll
+  for (int kt = 0; kt < KS_D; ++kt)
+#pragma unroll
+    for (int e = 0; e < KPL; ++e)
+      M::set(qf[kt], e, to_f32(sm.Qs[16 * tt + c][pi_idx(g, kt * KPL + e)]));
+
+  float gam[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) gam[r] = gexp(sm.Gs[16 * tt + 4 * g + r]);
+
+  const T *hf = (const T *)a.Hf + ch * Ge::H_ELEMS;
+  const T *nfp = (const T *)a.Nf + ch * Ge::W_ELEMS;
+  T *out = (T *)a.out;
+#pragma unroll 2
+  for (int jv = 0; jv < NT; ++jv) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < KS_D; ++kt) {
+      const frag fb = *reinterpret_cast<const frag *>(hf + (((int64_t)jv * KS_D + kt) * 64 + lane) * KPL);
+      acc = M::mma(qf[kt], fb, acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] *= gam[r];
+#pragma unroll
+    for (int kt = 0; kt < KS_C; ++kt) {
+      if ((kt * KPL) / 4 <= tt) {  // first j tile of this k-step
+        const frag fb = *reinterpret_cast<const frag *>(nfp + (((int64_t)jv * KS_C + kt) * 64 + lane) * KPL);
+        acc = M::mma(pf[kt], fb, acc);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tt + 4 * g + r;
+      if (t < len) out[((bos + t) * H + h) * D + 16 * jv + c] = from_f32<T>(a.scale * acc[r]);
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_output_t(const Args &a, hipStream_t s) {
+  const size_t smem = sizeof(OutSmem<T, D>);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)output_kernel<T, D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t blocks = a.cap * a.H;
+  if (blocks == 0) return hipSuccess;
+  output_kernel<T, D><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_output(const Args &a, hipStream_t s) {
+  if (a.dtype == GDN_BF16) {
+    if (a.D == 128) return launch_output_t<bf16, 128>(a, s);
+    if (a.D == 64) return launch_output_t<bf16, 64>(a, s);
+    return launch_output_t<bf16, 32>(a, s);
+  }
+  if (a.D == 128) return launch_output_t<float, 128>(a, s);
+  if (a.D == 64) return launch_output_t<float, 64>(a, s);
+  return launch_output_t<float, 32>(a, s);
+}
+
+}  // namespace gdn

@@ -4,9 +4,12 @@ This module only draws random numbers and rounds them to the storage dtype;
 it holds none of the method's arithmetic.  Both the HIP path's tests/bench and
 the CPU oracle take their inputs from here.
 
-Draw order per workload, from ``numpy.random.default_rng(seed)``: lengths,
-q, k, v, alpha, beta, initial state, pool slot permutation.  Values are drawn
-in fp32; bf16 workloads round them once (round to nearest even) and both sides
+Draws per workload: ``numpy.random.SeedSequence(seed)`` spawns one child per
+draw, in this order: lengths, q, k, v, alpha, beta, initial state, pool slot
+permutation.  Each child drives a PCG64 generator; normal arrays are drawn in
+blocks of 2**22 values, block b from the b-th grandchild of its child (so the
+values do not depend on how many threads draw them).  Values are drawn in
+fp32; bf16 workloads round them once (round to nearest even) and both sides
 use the rounded values.  "L2-normalised in the generator" divides each token's
 fp32 vector by its Euclidean norm before the rounding; that is part of the
 input recipe, not the kernel's in-kernel normalisation.
@@ -25,21 +28,75 @@ from typing import List, Optional
 import numpy as np
 
 
+def _round_bf16_inplace(x: np.ndarray) -> np.ndarray:
+    """Round a C-contiguous fp32 array to the nearest-even bf16 value in
+    place (finite values), block by block on threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    flat = x.reshape(-1).view(np.uint32)
+    step = 1 << 22
+
+    def work(s):
+        b = flat[s:s + step]
+        lsb = (b >> 16) & 1
+        b += 0x7FFF
+        b += lsb
+        b &= 0xFFFF0000
+
+    starts = range(0, flat.size, step)
+    if len(starts) > 1:
+        with ThreadPoolExecutor(16) as ex:
+            list(ex.map(work, starts))
+    else:
+        for s in starts:
+            work(s)
+    return x
+
+
 def round_bf16(x: np.ndarray) -> np.ndarray:
-    """fp32 -> nearest-even bf16, returned as fp32 holding the bf16 value."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
-    return b.astype(np.uint32).view(np.float32)
+    """fp32 -> nearest-even bf16, returned as a new fp32 array holding the
+    bf16 values (finite inputs)."""
+    return _round_bf16_inplace(np.array(x, dtype=np.float32, copy=True, order="C"))
 
 
-def _normal(rng, shape, dtype=np.float32):
-    return rng.standard_normal(size=shape, dtype=np.float32).astype(dtype)
+_BLOCK = 1 << 22
+
+
+def _normal(seq: np.random.SeedSequence, shape, std: float = 1.0) -> np.ndarray:
+    """fp32 N(0, std^2) array, drawn block by block (threads in parallel)."""
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty(shape, dtype=np.float32)
+    flat = out.reshape(-1)
+    nb = (flat.size + _BLOCK - 1) // _BLOCK
+    kids = seq.spawn(nb)
+
+    def work(b):
+        g = np.random.Generator(np.random.PCG64(kids[b]))
+        blk = flat[b * _BLOCK:(b + 1) * _BLOCK]
+        g.standard_normal(out=blk, dtype=np.float32)
+        if std != 1.0:
+            blk *= np.float32(std)
+
+    if nb > 1:
+        with ThreadPoolExecutor(min(16, nb)) as ex:
+            list(ex.map(work, range(nb)))
+    elif nb == 1:
+        work(0)
+    return out
+
+
+def _gen(seq: np.random.SeedSequence) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seq))
 
 
 def _unit_rows(x: np.ndarray) -> np.ndarray:
-    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
-    return (x / n).astype(np.float32)
+    """Divide each vector (last axis) by its Euclidean norm, block by block."""
+    out = np.empty_like(x, dtype=np.float32)
+    step = max(1, (1 << 22) // max(1, x.shape[-1] * x.shape[-2]))
+    for s in range(0, x.shape[0], step):
+        blk = x[s:s + step].astype(np.float64)
+        n = np.sqrt(np.sum(blk * blk, axis=-1, keepdims=True))
+        out[s:s + step] = (blk / n).astype(np.float32)
+    return out
 
 
 @dataclass
@@ -104,37 +161,36 @@ def make(seed: int, lengths, hq: int, hk: int, hv: int, D: int,
     """General seeded workload.  ``init`` is None (zero state), "seq" (one
     state per sequence) or "pool" (a pool of ``pool_size`` rows addressed by
     a random unique ``state_indices``)."""
-    rng = np.random.default_rng(seed)
+    kids = np.random.SeedSequence(seed).spawn(8)
     if draw_lengths is not None:
-        lengths = draw_lengths(rng)
+        lengths = draw_lengths(_gen(kids[0]))
     lengths = [int(x) for x in lengths]
     T = int(sum(lengths))
     H = max(hq, hv)
-    q = _normal(rng, (T, hq, D)) * qkv_std
-    k = _normal(rng, (T, hk, D)) * qkv_std
-    v = _normal(rng, (T, hv, D)) * qkv_std
+    q = _normal(kids[1], (T, hq, D), qkv_std)
+    k = _normal(kids[2], (T, hk, D), qkv_std)
+    v = _normal(kids[3], (T, hv, D), qkv_std)
     if normalise_in_generator:
         q, k = _unit_rows(q), _unit_rows(k)
     if gates:
         lo, hi = alpha_range
-        g = rng.uniform(lo, hi, size=(T, H)).astype(np.float32)
-        x = rng.standard_normal(size=(T, H)).astype(np.float32)
+        g = _gen(kids[4]).uniform(lo, hi, size=(T, H)).astype(np.float32)
+        x = _gen(kids[5]).standard_normal(size=(T, H)).astype(np.float32)
         beta = (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
     else:
         g = beta = None
     init_state = sidx = None
     if init == "seq":
-        init_state = (rng.standard_normal(size=(len(lengths), H, D, D),
-                                          dtype=np.float32) * init_std)
+        init_state = _normal(kids[6], (len(lengths), H, D, D), init_std)
     elif init == "pool":
         assert pool_size is not None and pool_size >= len(lengths)
-        init_state = (rng.standard_normal(size=(pool_size, H, D, D),
-                                          dtype=np.float32) * init_std)
-        sidx = rng.permutation(pool_size)[:len(lengths)].astype(np.int32)
+        init_state = _normal(kids[6], (pool_size, H, D, D), init_std)
+        sidx = _gen(kids[7]).permutation(pool_size)[:len(lengths)].astype(np.int32)
     if init_state is not None and init_dtype == "bf16":
-        init_state = round_bf16(init_state)
+        init_state = _round_bf16_inplace(init_state)
     if dtype == "bf16":
-        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+        q, k, v = (_round_bf16_inplace(q), _round_bf16_inplace(k),
+                   _round_bf16_inplace(v))
     cu = _cu(lengths, cu_dtype)
     ccs = None
     if checkpoint_every > 0:

@@ -1,0 +1,184 @@
+/*
+ * gdn_prefill.h -- C ABI of libgdn_prefill: the varlen chunked Gated Delta
+ * Rule prefill scan on AMD MI355X (gfx950).
+ *
+ * What is computed (gitcode "FlashInfer GDN Prefill 完全指南", sections
+ * "GDN prefill" and "API 全参数解析"; weigao.cc "GDN 与 Chunked Prefill",
+ * sections "GDN 是什么" and "块内 state 和块间 final state"): for every
+ * sequence i of a packed varlen batch and every sab head h,
+ *
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * with S a head_size x head_size fp32 state (keys x values) that starts from
+ * the given initial state (or zero), is processed in 64-token chunks, and
+ * whose final value is optionally written out.  g is alpha itself (the forget
+ * gate, default all ones), beta the update gate (default all ones), scale
+ * defaults to 1/sqrt(head_size).
+ *
+ * Conventions shared by every entry point:
+ *  - Device pointers unless a comment says "host".  The caller owns every
+ *    buffer; the library never allocates, frees or synchronises.  All work is
+ *    enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ *    call returns without waiting.  No device-to-host copy happens in a call.
+ *  - Return value: 0 on success, a negative GDN_ERR_* code when a host-side
+ *    check fails (then nothing is launched).  gdn_status_string() names codes.
+ *  - Data that only the device can check (cu_seqlens contents, state_indices
+ *    values, checkpoint_cu_starts contents) never causes an out-of-bounds
+ *    access; violations set GDN_STATUS_* bits in the optional device word
+ *    `status`, which every call overwrites (it needs no clearing).
+ */
+#ifndef GDN_PREFILL_H
+#define GDN_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+#define GDN_CHUNK 64 /* kernel chunk length in tokens */
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype;
+typedef enum { GDN_I32 = 0, GDN_I64 = 1 } gdn_itype;
+
+/* Host-side error codes (return values). */
+#define GDN_OK 0
+#define GDN_ERR_NULL -1          /* a required pointer is NULL */
+#define GDN_ERR_SHAPE -2         /* token/sequence/head counts or head size */
+#define GDN_ERR_HEAD_RATIO -3    /* illegal q/k/v head sharing */
+#define GDN_ERR_DTYPE -4         /* unsupported dtype or index type */
+#define GDN_ERR_CHECKPOINT -5    /* checkpoint arguments inconsistent */
+#define GDN_ERR_STATE -6         /* state / pool arguments inconsistent */
+#define GDN_ERR_MAX_SEQLEN -7    /* max_seqlen outside [ceil(T/N), T] */
+#define GDN_ERR_WORKSPACE -8     /* workspace missing or too small */
+#define GDN_ERR_STRIDES -9       /* state strides not positive/non-overlapping */
+#define GDN_ERR_DEVICE -10       /* current device is not gfx950 */
+#define GDN_ERR_LAUNCH -11       /* a kernel launch failed */
+
+/* Device status bits (written to *status by every call). */
+#define GDN_STATUS_CU_SEQLENS 1u        /* cu_seqlens not non-decreasing within [0, T] */
+#define GDN_STATUS_CHECKPOINT_STARTS 2u /* checkpoint_cu_starts != prefix sum of floor(len/n) */
+#define GDN_STATUS_STATE_INDEX 4u       /* a state index outside [0, pool_size) */
+#define GDN_STATUS_CHUNK_CAPACITY 8u    /* more chunks than the sync-free bound (never expected) */
+
+/*
+ * Parameters of one prefill call (gitcode, section "API 全参数解析"; the
+ * fields keep that section's parameter names).
+ *
+ * Shapes, all row-major and contiguous unless strides are given:
+ *   q [T, num_q_heads, D], k [T, num_k_heads, D], v [T, num_v_heads, D],
+ *   qkv_dtype F32 or BF16 (F16 is rejected with GDN_ERR_DTYPE for now).
+ *   H = num_sab_heads = max(num_q_heads, num_v_heads); legal head sharing:
+ *   (hq == hk and hv % hq == 0) or (hk == hv and hq % hk == 0); sab head h
+ *   reads q head h / (H / hq), k head h / (H / hk), v head h / (H / hv).
+ *   g, beta [T, H] fp32, or NULL for all ones.  g is alpha in (0, 1].
+ *   output [T, H, D] in qkv_dtype; rows outside every sequence are untouched.
+ *   States are [rows, H, D(v), D(k)]: element [n][h][v][k] is S[k][v]; the
+ *   four element strides are given (all zero = contiguous).  initial_state
+ *   may be NULL (zero).  state dtypes: F32, BF16 or F16.
+ *   state_indices [N] (or NULL): sequence i reads initial_state[idx[i]] and,
+ *   if output_final_state, writes output_state[idx[i]]; indices must be
+ *   unique (caller precondition, gitcode section "状态池"); output_state may
+ *   be the same memory as initial_state (in-place pool); pool_size bounds the
+ *   indices and is the row count of both pools.  Without state_indices,
+ *   initial_state and output_state have N rows.
+ *   checkpoint_every_n_tokens: 0 = off, else a positive multiple of 64;
+ *   state_checkpoints [checkpoint_rows, H, D, D] (contiguous; rows outside
+ *   [0, checkpoint_rows) are never written) and checkpoint_cu_starts
+ *   [N+1] are then both required; checkpoint j (1-based) of sequence i is the
+ *   state after j*n of its tokens, at row checkpoint_cu_starts[i] + j - 1.
+ *   max_seqlen: 0 = unknown; otherwise must satisfy ceil(T/N) <= max_seqlen
+ *   <= T (gitcode section "约束与注意点").
+ */
+typedef struct gdn_prefill_params {
+  int64_t total_tokens;   /* T >= 0 */
+  int32_t num_seqs;       /* N >= 0; with cu_seqlens NULL, N must be 1 */
+  int32_t num_q_heads, num_k_heads, num_v_heads;
+  int32_t head_size;      /* D in {32, 64, 128} */
+  int32_t qkv_dtype;      /* gdn_dtype */
+  const void *q, *k, *v;
+  const float *g, *beta;
+  int32_t has_scale;
+  float scale;
+  const void *cu_seqlens; /* [N+1], NULL = one sequence [0, T] */
+  int32_t cu_seqlens_type; /* gdn_itype */
+  int32_t use_qk_l2norm_in_kernel; /* x / sqrt(sum x^2 + 1e-6), fp32 sums */
+  void *output;
+  const void *initial_state;
+  int32_t initial_state_dtype;
+  int64_t initial_state_strides[4];
+  int32_t output_final_state;
+  void *output_state;
+  int32_t output_state_dtype;
+  int64_t output_state_strides[4];
+  const void *state_indices;
+  int32_t state_indices_type;
+  int64_t pool_size;
+  int32_t checkpoint_every_n_tokens;
+  void *state_checkpoints;
+  int32_t checkpoint_dtype;
+  int64_t checkpoint_rows;
+  const void *checkpoint_cu_starts;
+  int32_t checkpoint_cu_starts_type;
+  int64_t max_seqlen;
+  void *workspace;
+  size_t workspace_bytes;
+  int32_t *status;        /* optional device word */
+} gdn_prefill_params;
+
+/* ABI version (GDN_ABI_VERSION). */
+int gdn_abi_version(void);
+
+/* Static text for an error code (negative) or a status bit (positive). */
+const char *gdn_status_string(int code);
+
+/* Upper bound on the number of 64-token chunks of any batch with T tokens
+ * and N sequences, needing no look at cu_seqlens:
+ * floor((T + 63 * min(N, T)) / 64).  Host only. */
+int64_t gdn_max_chunks(int64_t total_tokens, int32_t num_seqs);
+
+/* Bytes of device workspace gdn_prefill() needs for these parameters (only
+ * the shape fields are read).  Host only; 0 for an invalid shape. */
+size_t gdn_prefill_workspace_size(const gdn_prefill_params *p);
+
+/* Every host-side check of gdn_prefill() except the device check, without
+ * touching the GPU.  Returns GDN_OK or a GDN_ERR_* code. */
+int gdn_validate_host(const gdn_prefill_params *p);
+
+/* The whole prefill: chunk-index build, intra-chunk pass, inter-chunk state
+ * pass (with checkpoints and final/pool write-back), output pass.
+ * Asynchronous on `stream`. */
+int gdn_prefill(const gdn_prefill_params *p, void *stream);
+
+/*
+ * The device-side chunk-index builder alone (weigao.cc, sections "chunked
+ * prefill 有两层含义" and "为什么 trace 里它可能看起来很贵": the flat chunk ->
+ * (sequence, chunk) table built on the device, with no device-to-host copy).
+ *   cu_seqlens [N+1] (int32 or int64 per cu_type).
+ *   chunk_indices [cap][2] int32: entry f = (sequence, chunk in sequence),
+ *     sequence-major; entries at f >= n_chunks are (-1, -1).
+ *     cap = gdn_max_chunks(total_tokens, num_seqs).
+ *   cu_chunks [N+1] int32: exclusive prefix sum of ceil(len_i / 64).
+ *   seq_starts [N+1] int32: the sequence starts actually used: cu_seqlens
+ *     clamped into [0, T] and made non-decreasing (running maximum), so the
+ *     table never exceeds cap even for invalid input (which also sets
+ *     GDN_STATUS_CU_SEQLENS in *status).  Equal to cu_seqlens when it is
+ *     valid.
+ *   n_chunks [1] int32.  status: optional device word.
+ * Every output buffer is caller-owned; cu_seqlens NULL means one sequence
+ * [0, T] (num_seqs must then be 1).
+ */
+int gdn_build_chunk_indices(const void *cu_seqlens, int32_t cu_type,
+                            int32_t num_seqs, int64_t total_tokens,
+                            int32_t *chunk_indices, int32_t *cu_chunks,
+                            int32_t *seq_starts, int32_t *n_chunks,
+                            int32_t *status, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_PREFILL_H */

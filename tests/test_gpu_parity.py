@@ -1,0 +1,279 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Relative L2 error per tensor: <= 1e-4 for fp32 inputs, <= 2e-2 for bf16
+inputs.  The chunk table and pool indexing are compared bit for bit.  The
+five named workloads run at their full sizes in the launch configuration the
+benchmark times; where the oracle would take too long (the long single
+sequence) it is evaluated on sampled heads.
+"""
+import numpy as np
+import pytest
+
+from gated_deltanet_chunked_varlen_amd import workloads as W
+from oracle import oracle
+from tests import gdn_testlib as tl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def _check(wl, gpu, orc, heads=None):
+    errs, tol = tl.compare(wl, gpu, orc, heads)
+    print(wl.name, {k: "%.3e" % v for k, v in errs.items()}, "tol", tol, flush=True)
+    for k, e in errs.items():
+        assert e <= tol, (k, e, tol)
+    return errs
+
+
+# --------------------------------------------------------------- chunk table
+
+CU_CASES = [
+    [0, 130, 150, 450],                      # the weigao.cc example
+    [0, 130, 150, 450, 450, 514, 515],       # ragged with an empty sequence
+    [0, 0, 0],                               # all empty
+    [0],                                     # no sequences
+    [0, 64, 128, 192],                       # exact multiples
+    [0, 1],                                  # a single token
+    [0, 262144],                             # one long sequence
+]
+
+
+@pytest.mark.parametrize("cu", CU_CASES + ["random_big"])
+@pytest.mark.parametrize("itype", ["int32", "int64"])
+def test_chunk_index_bitexact(cu, itype):
+    from gated_deltanet_chunked_varlen_amd import build_chunk_indices
+    if cu == "random_big":
+        rng = np.random.default_rng(5)
+        lens = rng.integers(0, 200, 2500)
+        lens[rng.random(2500) < 0.2] = 0
+        cu = np.concatenate([[0], np.cumsum(lens)])
+    cu = np.asarray(cu, dtype=np.int64)
+    T = int(cu[-1])
+    dev = torch.from_numpy(cu.astype(itype)).cuda()
+    table, cc, starts, n, st = build_chunk_indices(dev, T)
+    torch.cuda.synchronize()
+    want_t, want_cc, want_n = oracle.chunk_table(cu, 64)
+    assert int(n.item()) == want_n
+    assert int(st.item()) == 0
+    np.testing.assert_array_equal(cc.cpu().numpy(), want_cc)
+    np.testing.assert_array_equal(starts.cpu().numpy(), cu.astype(np.int32))
+    got = table.cpu().numpy()
+    np.testing.assert_array_equal(got[:want_n], want_t)
+    assert (got[want_n:] == -1).all()
+
+
+def test_chunk_index_flags_bad_cu_seqlens():
+    from gated_deltanet_chunked_varlen_amd import build_chunk_indices
+    cu = torch.tensor([0, 100, 50, 300, 200], dtype=torch.int32, device="cuda")
+    table, cc, starts, n, st = build_chunk_indices(cu, 250)
+    torch.cuda.synchronize()
+    assert int(st.item()) & 1
+    s = starts.cpu().numpy()
+    assert (np.diff(s) >= 0).all() and s[-1] <= 250 and s[0] == 0
+    assert int(n.item()) <= table.shape[0]
+
+
+# ------------------------------------------------------------- named configs
+
+def test_c1_single_small_fp32():
+    wl = W.c1_single_small()
+    gpu = tl.run_gpu(wl)
+    orc = tl.run_oracle(wl)
+    _check(wl, gpu, orc)
+    # elementwise, the tolerance 0539edu section 3.4 suggests
+    np.testing.assert_allclose(gpu["out"], orc["out"], rtol=1e-4, atol=1e-5)
+    np.testing.assert_allclose(gpu["final"], orc["final"], rtol=1e-4, atol=1e-5)
+
+
+def test_c2_two_by_2048():
+    wl = W.c2_two_by_2048()
+    _check(wl, tl.run_gpu(wl), tl.run_oracle(wl))
+
+
+def test_c3_ragged_pool_in_place():
+    wl = W.c3_ragged_pool()
+    gpu = tl.run_gpu(wl, status=True)
+    orc = tl.run_oracle(wl)
+    assert gpu["status"] == 0
+    _check(wl, gpu, orc)
+    # rows not addressed by state_indices are bitwise unchanged
+    idx = set(int(r) for r in wl.state_indices)
+    others = [r for r in range(wl.initial_state.shape[0]) if r not in idx]
+    np.testing.assert_array_equal(gpu["final"][others], gpu["pool_before"][others])
+    # the empty sequence keeps its state exactly
+    empty = int(wl.state_indices[3])
+    np.testing.assert_array_equal(gpu["final"][empty], gpu["pool_before"][empty])
+
+
+# ---------------------------------------------------------------- edge cases
+
+def _small(seed, lengths, dtype="bf16", hq=2, hk=2, hv=2, D=128, **kw):
+    kw.setdefault("l2norm_in_kernel", True)
+    return W.make(seed, lengths, hq, hk, hv, D, dtype, **kw)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("bf16", 32),
+                                     ("f32", 128), ("f32", 64), ("f32", 32)])
+def test_dtype_and_head_size(dtype, D):
+    wl = _small(11, [200, 64, 0, 65, 3], dtype=dtype, D=D, init="seq")
+    _check(wl, tl.run_gpu(wl), tl.run_oracle(wl))
+
+
+@pytest.mark.parametrize("hq,hk,hv", [(4, 2, 2), (2, 2, 6), (3, 3, 3)])
+def test_head_sharing(hq, hk, hv):
+    wl = _small(12, [100, 70], hq=hq, hk=hk, hv=hv)
+    _check(wl, tl.run_gpu(wl), tl.run_oracle(wl))
+
+
+def test_defaults_no_gates_no_scale():
+    wl = _small(13, [150, 40], gates=False, qkv_std=1.0)
+    _check(wl, tl.run_gpu(wl), tl.run_oracle(wl))
+
+
+def test_explicit_scale_and_no_l2norm():
+    wl = _small(14, [90], normalise_in_generator=True, l2norm_in_kernel=False,
+                scale=0.3)
+    _check(wl, tl.run_gpu(wl), tl.run_oracle(wl))
+
+
+def test_empty_batch_and_zero_lengths():
+    wl = _small(15, [0, 0, 0], init="seq")
+    gpu = tl.run_gpu(wl)
+    # no tokens: final state = initial state, converted to fp32
+    np.testing.assert_array_equal(gpu["final"], wl.initial_state.astype(np.float64))
+
+
+def test_int64_metadata_and_pool_not_in_place():
+    wl = _small(16, [33, 130, 7], init="pool", pool_size=9,
+                cu_dtype=np.int64)
+    wl.state_indices = wl.state_indices.astype(np.int64)
+    gpu = tl.run_gpu(wl)
+    orc = tl.run_oracle(wl)
+    _check(wl, gpu, orc)
+
+
+@pytest.mark.parametrize("sdt", ["bf16", "f16"])
+def test_state_dtypes(sdt):
+    wl = _small(17, [300, 20], init="seq", init_dtype="bf16")
+    wl.final_state_dtype = sdt
+    gpu = tl.run_gpu(wl)
+    orc = tl.run_oracle(wl)
+    _check(wl, gpu, orc)
+
+
+def test_strided_states():
+    """Initial and final states as non-contiguous views ([v][k] order kept,
+    heads and rows interleaved differently)."""
+    wl = _small(18, [140, 64], init="seq")
+    H, D, N = wl.H, wl.D, wl.N
+    base = torch.from_numpy(np.ascontiguousarray(
+        wl.initial_state.transpose(1, 0, 2, 3))).cuda()       # [H, N, V, K]
+    init = base.permute(1, 0, 2, 3)                            # [N, H, V, K] view
+    outbuf = torch.zeros((H, D, D, N), dtype=torch.float32, device="cuda")
+    outst = outbuf.permute(3, 0, 1, 2)                         # [N, H, V, K] view
+    gpu = tl.run_gpu(wl, initial_state=init, output_state=outst)
+    orc = tl.run_oracle(wl)
+    _check(wl, dict(gpu, final=outst.cpu().numpy().astype(np.float64)), orc)
+
+
+def test_checkpoints_every_64_and_bf16_checkpoint_rows():
+    wl = _small(19, [300, 64, 130, 0], init="seq", checkpoint_every=64)
+    _check(wl, tl.run_gpu(wl), tl.run_oracle(wl))
+
+
+def test_determinism_bitwise():
+    wl = W.c3_ragged_pool()
+    a = tl.run_gpu(wl)
+    b = tl.run_gpu(wl)
+    np.testing.assert_array_equal(a["out"], b["out"])
+    np.testing.assert_array_equal(a["final"], b["final"])
+
+
+def test_continuation_split_runs():
+    """Running a sequence in two calls, passing the first call's final state
+    as the second's initial state, matches one call (weigao.cc, section
+    "chunked prefill 有两层含义": scheduler-level chunked prefill)."""
+    wl = _small(20, [500], init="seq")
+    full = tl.run_gpu(wl)
+    cut = 130
+    a = W.make(20, [500], 2, 2, 2, 128, "bf16", l2norm_in_kernel=True, init="seq")
+    first = W.Workload(**{**a.__dict__})
+    first.q, first.k, first.v = a.q[:cut], a.k[:cut], a.v[:cut]
+    first.g, first.beta = a.g[:cut], a.beta[:cut]
+    first.cu_seqlens = np.array([0, cut], dtype=np.int32)
+    r1 = tl.run_gpu(first)
+    second = W.Workload(**{**a.__dict__})
+    second.q, second.k, second.v = a.q[cut:], a.k[cut:], a.v[cut:]
+    second.g, second.beta = a.g[cut:], a.beta[cut:]
+    second.cu_seqlens = np.array([0, 500 - cut], dtype=np.int32)
+    second.initial_state = r1["final"].astype(np.float32)
+    r2 = tl.run_gpu(second)
+    out = np.concatenate([r1["out"], r2["out"]])
+    assert tl.rel_l2(out, full["out"]) < 2e-2
+    assert tl.rel_l2(r2["final"], full["final"]) < 2e-2
+
+
+# ------------------------------------------------------- device status words
+
+def test_status_bad_state_index_writes_nothing():
+    wl = _small(21, [70, 40], init="pool", pool_size=4, in_place_pool=True)
+    wl.state_indices = np.array([1, 9], dtype=np.int32)    # 9 is out of range
+    gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] & 4
+    for r in (0, 2, 3):
+        np.testing.assert_array_equal(gpu["final"][r], gpu["pool_before"][r])
+
+
+def test_status_checkpoint_starts_mismatch():
+    wl = _small(22, [300, 130], init="seq", checkpoint_every=64)
+    wl.checkpoint_cu_starts = wl.checkpoint_cu_starts.copy()
+    wl.checkpoint_cu_starts[1] += 1                         # inconsistent
+    gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] & 2
+
+
+def test_host_errors_raise_before_launch():
+    from gated_deltanet_chunked_varlen_amd import chunk_gated_delta_rule
+    wl = _small(23, [64, 64])
+    d = tl.to_device(wl)
+    with pytest.raises(ValueError):
+        chunk_gated_delta_rule(d["q"], d["k"], d["v"], cu_seqlens=d["cu_seqlens"],
+                               checkpoint_every_n_tokens=100,
+                               state_checkpoints=torch.zeros(4, 2, 128, 128, device="cuda"),
+                               checkpoint_cu_starts=torch.zeros(3, dtype=torch.int32, device="cuda"))
+    with pytest.raises(ValueError):
+        chunk_gated_delta_rule(d["q"], d["k"], d["v"], cu_seqlens=d["cu_seqlens"],
+                               max_seqlen=10)
+    with pytest.raises(ValueError):
+        chunk_gated_delta_rule(d["q"], d["k"], d["v"], cu_seqlens=d["cu_seqlens"],
+                               output_final_state=True,
+                               state_indices=torch.tensor([0, 1], dtype=torch.int32, device="cuda"),
+                               initial_state=torch.zeros(4, 2, 128, 128, device="cuda"))
+
+
+# ------------------------------------------------- large named configs (last)
+
+def test_c4_gva_checkpoints():
+    wl = W.c4_gva_checkpoints()
+    heads = [0, 1, 17, 31]
+    gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] == 0
+    orc = tl.run_oracle(wl, heads=heads)
+    _check(wl, gpu, orc, heads=heads)
+
+
+@pytest.mark.timeout(600)
+def test_c5_long_single_sampled_heads():
+    wl = W.c5_long_single()
+    heads = [0, 31]
+    gpu = tl.run_gpu(wl)
+    orc = tl.run_oracle(wl, heads=heads)
+    _check(wl, gpu, orc, heads=heads)

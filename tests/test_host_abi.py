@@ -1,0 +1,166 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol the header
+declares, and its host-side checks return the documented codes.  No compute
+call is made (no GPU here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "gdn_prefill.h")
+
+
+def _lib():
+    from gated_deltanet_chunked_varlen_amd import _native
+    return _native
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(gdn_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_symbols_exported():
+    nat = _lib()
+    L = nat.lib()
+    declared = declared_functions()
+    assert set(declared) == set(nat.EXPORTS), declared
+    for name in declared:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", nat.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (gdn_\w+)", out))
+    assert set(declared) <= exported
+
+
+def test_abi_version_and_strings():
+    nat = _lib()
+    assert nat.lib().gdn_abi_version() == 1
+    for code in list(nat.ERRORS) + [1, 2, 4, 8]:
+        assert nat.status_string(code) != "unknown code"
+
+
+@pytest.mark.parametrize("T,N,want", [
+    (0, 3, 0), (128, 1, 2), (130, 1, 3), (515, 6, 13), (4096, 2, 65),
+    (262144, 1, 4096), (5, 10, 5)])
+def test_max_chunks_bound(T, N, want):
+    assert _lib().lib().gdn_max_chunks(T, N) == want
+
+
+def test_max_chunks_bounds_every_batch():
+    from oracle import oracle
+    L = _lib().lib()
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        N = int(rng.integers(1, 12))
+        lens = rng.integers(0, 300, N)
+        lens[rng.random(N) < 0.3] = 0
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        n = oracle.chunk_table(cu, 64)[2]
+        assert n <= L.gdn_max_chunks(int(cu[-1]), N)
+
+
+def _params(**kw):
+    nat = _lib()
+    p = nat.Params()
+    p.total_tokens = kw.get("T", 128)
+    p.num_seqs = kw.get("N", 1)
+    p.num_q_heads = kw.get("hq", 4)
+    p.num_k_heads = kw.get("hk", 4)
+    p.num_v_heads = kw.get("hv", 4)
+    p.head_size = kw.get("D", 128)
+    p.qkv_dtype = kw.get("dtype", nat.GDN_BF16)
+    fake = ctypes.c_void_p(0x1000)
+    p.q = p.k = p.v = p.output = fake
+    p.cu_seqlens = fake if kw.get("cu", True) else None
+    p.cu_seqlens_type = nat.GDN_I32
+    for f, v in kw.get("extra", {}).items():
+        setattr(p, f, v)
+    return p
+
+
+def _validate(p, with_ws=True):
+    nat = _lib()
+    L = nat.lib()
+    if with_ws:
+        need = L.gdn_prefill_workspace_size(ctypes.byref(p))
+        p.workspace = ctypes.c_void_p(0x2000)
+        p.workspace_bytes = need
+    return L.gdn_validate_host(ctypes.byref(p))
+
+
+def code(name):
+    return _lib().ERR_CODE[name]
+
+
+def test_validate_ok_and_workspace():
+    nat = _lib()
+    p = _params(T=4096, N=2, hq=16, hk=16, hv=16)
+    assert _validate(p) == 0
+    need = nat.lib().gdn_prefill_workspace_size(ctypes.byref(p))
+    # 65 chunks x 16 heads x (4 blocks of 64x128 + 128x128) bf16 + G
+    assert need >= 65 * 16 * (4 * 64 * 128 * 2 + 128 * 128 * 2 + 64 * 4)
+    p.workspace_bytes = need - 1
+    assert nat.lib().gdn_validate_host(ctypes.byref(p)) == code("GDN_ERR_WORKSPACE")
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(D=96), "GDN_ERR_SHAPE"),
+    (dict(T=-1), "GDN_ERR_SHAPE"),
+    (dict(N=2, cu=False), "GDN_ERR_SHAPE"),
+    (dict(hq=4, hk=2, hv=4), "GDN_ERR_HEAD_RATIO"),
+    (dict(hq=4, hk=4, hv=6), "GDN_ERR_HEAD_RATIO"),
+    (dict(dtype=2), "GDN_ERR_DTYPE"),
+    (dict(dtype=7), "GDN_ERR_DTYPE"),
+    (dict(extra=dict(q=None)), "GDN_ERR_NULL"),
+    (dict(extra=dict(checkpoint_every_n_tokens=100,
+                     state_checkpoints=ctypes.c_void_p(8),
+                     checkpoint_cu_starts=ctypes.c_void_p(8))), "GDN_ERR_CHECKPOINT"),
+    (dict(extra=dict(checkpoint_every_n_tokens=64,
+                     state_checkpoints=ctypes.c_void_p(8))), "GDN_ERR_CHECKPOINT"),
+    (dict(extra=dict(checkpoint_every_n_tokens=64)), "GDN_ERR_CHECKPOINT"),
+    (dict(extra=dict(output_final_state=1)), "GDN_ERR_STATE"),
+    (dict(extra=dict(state_indices=ctypes.c_void_p(8), pool_size=0)), "GDN_ERR_STATE"),
+    (dict(T=100, N=4, extra=dict(max_seqlen=24)), "GDN_ERR_MAX_SEQLEN"),
+    (dict(T=100, N=4, extra=dict(max_seqlen=101)), "GDN_ERR_MAX_SEQLEN"),
+    (dict(extra=dict(max_seqlen=-1)), "GDN_ERR_MAX_SEQLEN"),
+])
+def test_validate_errors(kw, err):
+    assert _validate(_params(**kw)) == code(err)
+
+
+def test_validate_accepts_legal_variants():
+    nat = _lib()
+    assert _validate(_params(hq=8, hk=4, hv=4)) == 0           # GQA
+    assert _validate(_params(hq=4, hk=4, hv=12)) == 0          # GVA
+    assert _validate(_params(T=100, N=4, extra=dict(max_seqlen=25))) == 0
+    assert _validate(_params(T=0, N=3)) == 0                    # empty batch
+    assert _validate(_params(dtype=nat.GDN_F32, D=32)) == 0
+
+
+def test_validate_strides():
+    nat = _lib()
+    H, D, N = 4, 128, 1
+    ok = nat._i64x4(H * D * D, D * D, D, 1)
+    transposed = nat._i64x4(H * D * D, D * D, 1, D)
+    overlap = nat._i64x4(H * D * D, D, D, 1)
+    negative = nat._i64x4(H * D * D, D * D, D, -1)
+    for strides, want in ((ok, 0), (transposed, 0),
+                          (overlap, code("GDN_ERR_STRIDES")),
+                          (negative, code("GDN_ERR_STRIDES"))):
+        p = _params(extra=dict(initial_state=ctypes.c_void_p(8),
+                               initial_state_dtype=nat.GDN_F32,
+                               initial_state_strides=strides))
+        assert _validate(p) == want
+
+
+def test_workspace_size_zero_for_bad_shape():
+    nat = _lib()
+    p = _params(D=48)
+    assert nat.lib().gdn_prefill_workspace_size(ctypes.byref(p)) == 0
