@@ -1,0 +1,377 @@
+#!/usr/bin/env python3
+"""Benchmark of the varlen chunked Gated Delta Rule prefill on one MI355X.
+
+A step is one full ``gdn_prefill`` call (chunk-index build, intra-chunk pass,
+state pass, output pass, all heads) over one batch of seeded synthetic input
+already resident in HBM; outputs and workspace are allocated once.  The
+default workload is 2 sequences x 2048 tokens, 16 heads, head size 128, bf16
+q/k/v with in-kernel q/k L2 normalisation (the shape of gitcode "FlashInfer
+GDN Prefill 完全指南", section "基础用法").
+
+Prints one JSON line with the throughput (tokens/s over all heads), the
+roofline position of the dominant kernel (timed live with HIP events recorded
+around it on the call's stream) and the CPU oracle's throughput on the same
+workload (a bounded number of repetitions on this host's cores).
+
+    python bench.py [--steps K] [--warmup W] [--workload c2]
+    python bench.py --copy-calibration      # plain 1 GiB copies, for counters
+    python bench.py --summarize <workload> <rocprofv3 output dirs...> <command>
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak
+FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 matrix peak
+PHASES = ["chunk_index", "intra", "state", "output"]
+KERNEL_SOURCES = {
+    "chunk_index": "k0_chunk_index.hip", "intra": "k1_intra.hip",
+    "state": "k2_state.hip", "output": "k3_output.hip",
+}
+
+
+def per_token_head_bytes(wl, phase):
+    """Algorithmic HBM bytes per (token, sab head) of each phase (fp32 gates,
+    q/k/v/o and intermediates in the compute dtype of width e).
+
+    intra : reads k, v, g, beta; writes W, Ktilde, U (64 x D each per
+            chunk-head) and the 64 cumulative log gates
+    state : reads W, Ktilde, U, G_last; writes the chunk-start state
+            (D x D per chunk-head) and the new values N (64 x D)
+    output: reads q, k, chunk-start state, N, G; writes o
+    Shared q/k/v heads are counted once per source head.
+    """
+    D, H = wl.D, wl.H
+    e = 2 if wl.dtype == "bf16" else 4
+    hq, hk, hv = wl.q.shape[1], wl.k.shape[1], wl.v.shape[1]
+    qf, kf, vf = hq / H, hk / H, hv / H
+    st = D * D * e / 64.0          # chunk-start state per token
+    if phase == "intra":
+        return (kf + vf) * D * e + 8 + 3 * D * e + 4
+    if phase == "state":
+        return 3 * D * e + 4.0 / 64 + st + D * e
+    if phase == "output":
+        return (qf + kf) * D * e + st + D * e + 4 + D * e
+    return 0.0
+
+
+FLOPS_PER_TOKEN_HEAD = lambda D: 2 * (5 * 64 * D + 3 * D * D)   # eight chunk GEMMs
+
+
+def hip():
+    L = ctypes.CDLL("libamdhip64.so.7")
+    L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return L
+
+
+def new_event(L):
+    ev = ctypes.c_void_p()
+    if L.hipEventCreate(ctypes.byref(ev)) != 0:
+        raise RuntimeError("hipEventCreate failed")
+    return ev
+
+
+def elapsed_ms(L, a, b):
+    ms = ctypes.c_float()
+    if L.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+        raise RuntimeError("hipEventElapsedTime failed")
+    return float(ms.value)
+
+
+def source_hash(name):
+    path = os.path.join(ROOT, "gated_deltanet_chunked_varlen_amd", "csrc", name)
+    h = hashlib.sha256()
+    for p in (path, os.path.join(os.path.dirname(path), "gdn_common.h")):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(phase, workload):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        db = json.load(f)
+    rec = db.get("%s/%s" % (phase, workload))
+    if not rec or rec.get("source_hash") != source_hash(KERNEL_SOURCES[phase]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle as it stands, timed on this host: the whole workload,
+    repeated until ``seconds`` have passed (at least once)."""
+    from oracle import oracle
+    from tests import gdn_testlib as tl
+    prob = tl.oracle_problem(wl)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.token(prob)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    items = wl.N * wl.H
+    return {"value": wl.T * reps / dt, "unit": "tokens/s",
+            "cores": min(oracle.num_threads(), items), "kind": "oracle",
+            "sample": "whole workload (%d tokens x %d heads), fp64 token "
+                      "recurrence, %d repetition(s) in %.1f s" % (
+                          wl.T, wl.H, reps, dt)}
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+
+
+PROF_KERNELS = {"chunk_index": "chunk_index_kernel", "intra": "intra_kernel",
+                "state": "state_kernel", "output": "output_kernel"}
+
+
+def _one(d, pat):
+    import glob
+    hits = glob.glob(os.path.join(d, "**", pat), recursive=True)
+    if not hits:
+        raise SystemExit("no %s under %s" % (pat, d))
+    return hits[0]
+
+
+def _counters(d):
+    import collections
+    import csv
+    out = collections.defaultdict(list)
+    for r in csv.DictReader(open(_one(d, "*counter_collection.csv"))):
+        out[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return out
+
+
+def _by_phase(table):
+    res = {}
+    for ph, key in PROF_KERNELS.items():
+        vals = [v for name, vs in table.items() if key in name for v in vs]
+        if vals:
+            res[ph] = sum(vals) / len(vals)
+    return res
+
+
+def summarize(argv):
+    """Write profiles/<workload>_kernels.md and update profiles/traffic.json
+    from rocprofv3 CSV output: argv = workload, kernel-trace dir, FETCH_SIZE
+    dir, WRITE_SIZE dir, copy FETCH dir, copy WRITE dir, command text.
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what the same
+    counters read for the plain 1 GiB copy of --copy-calibration."""
+    import collections
+    import csv
+    import glob
+    wname, kdir, fdir, wdir, cfdir, cwdir = argv[:6]
+    cmd = " ".join(argv[6:])
+    stats = list(csv.DictReader(open(_one(kdir, "*kernel_stats.csv"))))
+    fetch, write = _by_phase(_counters(fdir)), _by_phase(_counters(wdir))
+    cal_bytes = 1 << 30
+    cf = [v for n, vs in _counters(cfdir).items() if "copyBuffer" in n for v in vs]
+    cw = [v for n, vs in _counters(cwdir).items() if "copyBuffer" in n for v in vs]
+    f_scale = cal_bytes / (sum(cf) / len(cf) * 1024.0)
+    w_scale = cal_bytes / (sum(cw) / len(cw) * 1024.0)
+    lines = ["# Kernel trace and HBM counters: %s" % wname, "",
+             "Command (kernel trace):", "", "    " + cmd, "",
+             "| kernel | calls | avg us | min us | max us | share |",
+             "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append("| %s | %s | %.2f | %.2f | %.2f | %s%% |" % (
+            r["Name"][:60], r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, r["Percentage"]))
+    lines += ["", "Counter passes: the same bench command under `rocprofv3 --pmc "
+              "FETCH_SIZE` and `--pmc WRITE_SIZE` (`--steps 20 --warmup 5`).",
+              "Calibration (`bench.py --copy-calibration`, 1 GiB copy): FETCH_SIZE "
+              "reads %.1f KiB -> scale %.4f; WRITE_SIZE reads %.1f KiB -> scale %.4f." % (
+                  sum(cf) / len(cf), f_scale, sum(cw) / len(cw), w_scale), "",
+              "| kernel | FETCH KiB | WRITE KiB | HBM bytes/launch (scaled) |",
+              "|---|---|---|---|"]
+    db_path = os.path.join(ROOT, "profiles", "traffic.json")
+    db = json.load(open(db_path)) if os.path.exists(db_path) else {}
+    for ph in PROF_KERNELS:
+        if ph in fetch and ph in write:
+            b = fetch[ph] * 1024 * f_scale + write[ph] * 1024 * w_scale
+            lines.append("| %s | %.1f | %.1f | %.4g |" % (ph, fetch[ph], write[ph], b))
+            db["%s/%s" % (ph, wname)] = {
+                "bytes_per_launch": b, "fetch_kib": fetch[ph], "write_kib": write[ph],
+                "fetch_scale": f_scale, "write_scale": w_scale,
+                "source_hash": source_hash(KERNEL_SOURCES[ph])}
+    json.dump(db, open(db_path, "w"), indent=1, sort_keys=True)
+    out = os.path.join(ROOT, "profiles", "%s_kernels.md" % wname)
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
+def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
+        summarize(sys.argv[2:])
+        return
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2",
+                    help="c2 (default, the headline); c1..c5 for analysis")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py: this build runs on one GPU only (the state pass "
+                  "shards by sequence and head without communication; see the "
+                  "design notes); --gpus %d is not supported" % args.gpus,
+                  file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    from gated_deltanet_chunked_varlen_amd import workloads as W
+    from gated_deltanet_chunked_varlen_amd import api
+    from gated_deltanet_chunked_varlen_amd import _native as nat
+    from tests import gdn_testlib as tl
+
+    wl = W.WORKLOADS[args.workload]()
+    d = tl.to_device(wl)
+    H, D, N, T = wl.H, wl.D, wl.N, wl.T
+    kw = dict(g=d["g"], beta=d["beta"], scale=wl.scale, cu_seqlens=d["cu_seqlens"],
+              use_qk_l2norm_in_kernel=wl.l2norm_in_kernel,
+              output_final_state=wl.output_final_state)
+    if wl.state_indices is not None:
+        kw.update(initial_state=d["initial_state"], state_indices=d["state_indices"],
+                  output_state=d["initial_state"])
+    else:
+        kw.update(initial_state=d["initial_state"])
+    if wl.checkpoint_every > 0:
+        rows = int(wl.checkpoint_cu_starts[-1])
+        kw.update(state_checkpoints=torch.empty((rows, H, D, D), device="cuda"),
+                  checkpoint_cu_starts=d["checkpoint_cu_starts"],
+                  checkpoint_every_n_tokens=wl.checkpoint_every)
+    p, out, outst = api.make_params(d["q"], d["k"], d["v"], **kw)
+    need = api.workspace_size(p)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    p.workspace, p.workspace_bytes = ctypes.c_void_p(ws.data_ptr()), need
+    lib = nat.lib()
+    L = hip()
+    stream = torch.cuda.current_stream().cuda_stream
+    none5 = (ctypes.c_void_p * 5)()
+
+    def call(evs=none5):
+        rc = lib.gdn_prefill_timed(ctypes.byref(p), ctypes.c_void_p(stream), evs)
+        if rc != 0:
+            raise RuntimeError(nat.status_string(rc))
+
+    # warm-up, with every phase timed to find the dominant kernel
+    ev = [[new_event(L) for _ in range(5)] for _ in range(max(args.warmup, 1))]
+    for i in range(max(args.warmup, 1)):
+        call((ctypes.c_void_p * 5)(*ev[i]))
+    torch.cuda.synchronize()
+    phase_ms = {ph: 0.0 for ph in PHASES}
+    for i in range(max(args.warmup, 1)):
+        for j, ph in enumerate(PHASES):
+            phase_ms[ph] += elapsed_ms(L, ev[i][j], ev[i][j + 1])
+    phase_ms = {ph: v / max(args.warmup, 1) for ph, v in phase_ms.items()}
+    dom = max(PHASES, key=lambda ph: phase_ms[ph])
+    di = PHASES.index(dom)
+
+    # timed region: exactly K steps, events around the dominant kernel
+    K = args.steps
+    pairs = [(new_event(L), new_event(L)) for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        e5 = (ctypes.c_void_p * 5)()
+        e5[di], e5[di + 1] = pairs[i][0], pairs[i][1]
+        call(e5)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(stop)
+    dom_ms = sum(elapsed_ms(L, a, b) for a, b in pairs) / K
+    for row in ev:
+        for e in row:
+            L.hipEventDestroy(e)
+    for a, b in pairs:
+        L.hipEventDestroy(a)
+        L.hipEventDestroy(b)
+
+    ms_step = ms_total / K
+    tokens_per_s = T * K / (ms_total / 1e3)
+    flops = T * H * FLOPS_PER_TOKEN_HEAD(D)
+    tflops = flops / (ms_step / 1e3) / 1e12
+    peak_mm = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    bytes_launch = per_token_head_bytes(wl, dom) * T * H
+    achieved = bytes_launch / (dom_ms / 1e3) / 1e9
+    traffic = load_traffic(dom, wl.name)
+
+    res = {
+        "metric": "GDN prefill tokens/s (all heads) + % of MI355X bf16 MFMA peak, H=16 D=128",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded numpy draws, see workloads.py)",
+        "config": {"workload": wl.name, "num_seqs": N, "seq_lens": wl.lengths,
+                   "total_tokens": T, "num_q_heads": int(wl.q.shape[1]),
+                   "num_k_heads": int(wl.k.shape[1]), "num_v_heads": int(wl.v.shape[1]),
+                   "head_size": D, "qk_l2norm_in_kernel": wl.l2norm_in_kernel,
+                   "parallelism": "single GPU"},
+        "tflops_canonical": tflops,
+        "mfma_peak_frac": tflops / peak_mm,
+        "phase_ms_warmup": phase_ms,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "avg_launch_ms": dom_ms,
+                     "algorithmic_bytes_per_launch": bytes_launch},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -218,7 +218,7 @@ int gdn_build_chunk_indices(const void *cu_seqlens, int32_t cu_type, int32_t num
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
-int gdn_prefill(const gdn_prefill_params *p, void *stream) {
+static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *events) {
   int rc = gdn_validate_host(p);
   if (rc != GDN_OK) return rc;
   rc = check_device();
@@ -280,14 +280,32 @@ int gdn_prefill(const gdn_prefill_params *p, void *stream) {
   a.status = p->status;
   if (a.ck_every > 0 && !a.ck) a.ck_every = 0;
 
-  hipError_t e = launch_chunk_index(p->cu_seqlens, p->cu_seqlens_type, a.N, a.T, a.cap,
-                                    a.chunk_idx, a.cu_chunks, a.seq_bos, a.n_chunks, a.status,
-                                    a.ck_every > 0 ? a.ck_cs : nullptr, a.ck_cs_type, a.ck_every,
-                                    a.sidx, a.sidx_type, a.pool_rows, s);
+  auto mark = [&](int i) -> hipError_t {
+    if (events && events[i]) return hipEventRecord((hipEvent_t)events[i], s);
+    return hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e == hipSuccess)
+    e = launch_chunk_index(p->cu_seqlens, p->cu_seqlens_type, a.N, a.T, a.cap, a.chunk_idx,
+                           a.cu_chunks, a.seq_bos, a.n_chunks, a.status,
+                           a.ck_every > 0 ? a.ck_cs : nullptr, a.ck_cs_type, a.ck_every,
+                           a.sidx, a.sidx_type, a.pool_rows, s);
+  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess && a.cap > 0) e = launch_intra(a, s);
+  if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_state(a, s);
+  if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess && a.cap > 0) e = launch_output(a, s);
+  if (e == hipSuccess) e = mark(4);
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+int gdn_prefill(const gdn_prefill_params *p, void *stream) {
+  return prefill_impl(p, stream, nullptr);
+}
+
+int gdn_prefill_timed(const gdn_prefill_params *p, void *stream, void *const events[5]) {
+  return prefill_impl(p, stream, events);
 }
 
 }  // extern "C"

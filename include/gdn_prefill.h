@@ -153,6 +153,14 @@ int gdn_validate_host(const gdn_prefill_params *p);
  * Asynchronous on `stream`. */
 int gdn_prefill(const gdn_prefill_params *p, void *stream);
 
+/* gdn_prefill() with phase markers: events[i] (a hipEvent_t, or NULL to
+ * skip) is recorded on `stream` just before phase i -- 0 chunk-index build,
+ * 1 intra-chunk pass, 2 state pass, 3 output pass -- and events[4] after the
+ * last, so hipEventElapsedTime(events[i], events[i + 1]) times phase i.  The
+ * computation is exactly that of gdn_prefill().  events is a host array. */
+int gdn_prefill_timed(const gdn_prefill_params *p, void *stream,
+                      void *const events[5]);
+
 /*
  * The device-side chunk-index builder alone (weigao.cc, sections "chunked
  * prefill 有两层含义" and "为什么 trace 里它可能看起来很贵": the flat chunk ->
