@@ -31,6 +31,10 @@ typedef __bf16 bf16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+// 16-byte register vector; HIP's uint4 is a struct of unions that keeps
+// arrays of it out of registers, this native vector type does not.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
 
 constexpr int kChunk = 64;
 constexpr float kNormEps = 1e-6f;
@@ -55,6 +59,11 @@ template <> struct Mfma<bf16> {
   }
   static __device__ __forceinline__ void set(frag &f, int e, float x) { f[e] = (bf16)x; }
   static __device__ __forceinline__ float get(const frag &f, int e) { return (float)f[e]; }
+  // KPL consecutive fp32 values -> one operand fragment (packed conversions)
+  static __device__ __forceinline__ frag pack(const float *x) {
+    const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+    return __builtin_convertvector(v, bf16x8);
+  }
 };
 
 template <> struct Mfma<float> {
@@ -65,6 +74,7 @@ template <> struct Mfma<float> {
   }
   static __device__ __forceinline__ void set(frag &f, int, float x) { f = x; }
   static __device__ __forceinline__ float get(const frag &f, int) { return f; }
+  static __device__ __forceinline__ frag pack(const float *x) { return x[0]; }
 };
 
 // Contraction index of slot s in lane group g (see the header comment).
@@ -73,8 +83,10 @@ __device__ __forceinline__ int pi_idx(int g, int s) {
 }
 
 // ---------------------------------------------------------------------------
-// Workspace geometry.  Everything per (flat chunk f, sab head h); ch = f*H + h.
-//   Wf : [ch][4 row tiles][D/(4K) ksteps][64][K]      W, contraction dk in pi order
+// Workspace geometry.  Everything per (flat chunk f, sab head h), stored
+// head-major: ch = h * cap + f (cap = flat-chunk capacity), so the chunks of
+// one head that the state pass walks through sit next to each other.
+//   Wf : [ch][4 row tiles][D/(4K) ksteps][64][K]      -W, contraction dk in pi order
 //   Kf : [ch][D/16 row tiles][64/(4K)][64][K]          Ktilde^T, contraction t in pi order
 //   Uf : [ch][D/16 dv tiles][4 row tiles][64][4]       U in result layout
 //   Gw : [ch][64] fp32                                 cumulative log gate
@@ -82,6 +94,10 @@ __device__ __forceinline__ int pi_idx(int g, int s) {
 //   Nf : [ch][D/16 dv tiles][64/(4K)][64][K]           new values, t in pi order
 // (K = KPL.)  Each block is 64*D elements except Gw (64) and Hf (D*D).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t ws_index(int f, int h, int64_t cap) {
+  return (int64_t)h * cap + f;
+}
+
 template <typename T, int D> struct Geo {
   static constexpr int KPL = Mfma<T>::KPL;
   static constexpr int NT = D / 16;             // 16-wide tiles along D

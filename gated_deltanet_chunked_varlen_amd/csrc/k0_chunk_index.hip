@@ -21,6 +21,7 @@
 namespace gdn {
 
 constexpr int kK0Threads = 1024;
+constexpr int kK0Lds = 4096;  // sequences whose starts / chunk offsets stay in LDS
 
 __device__ __forceinline__ int64_t load_index(const void *p, int type, int64_t i) {
   return type == GDN_I64 ? ((const int64_t *)p)[i] : (int64_t)((const int32_t *)p)[i];
@@ -64,6 +65,8 @@ chunk_index_kernel(const void *cu, int cu_type, int32_t N, int64_t T, int64_t ca
   __shared__ int64_t sh_wave[kK0Threads / 64];
   __shared__ int64_t sh_carry[2];
   __shared__ unsigned sh_status;
+  __shared__ int32_t sh_bos[kK0Lds + 1], sh_cc[kK0Lds + 1];
+  const bool small = N <= kK0Lds;
   const int tid = threadIdx.x;
   if (tid == 0) { sh_status = 0u; sh_carry[0] = 0; sh_carry[1] = 0; }
   __syncthreads();
@@ -82,7 +85,10 @@ chunk_index_kernel(const void *cu, int cu_type, int32_t N, int64_t T, int64_t ca
     const int64_t carry = sh_carry[0];
     int64_t m = block_scan<true>(x, sh_wave);
     m = m > carry ? m : carry;
-    if (i <= N) seq_bos[i] = (int32_t)m;
+    if (i <= N) {
+      seq_bos[i] = (int32_t)m;
+      if (small) sh_bos[i] = (int32_t)m;
+    }
     if (tid == kK0Threads - 1) sh_carry[0] = m;
     __syncthreads();
   }
@@ -96,7 +102,8 @@ chunk_index_kernel(const void *cu, int cu_type, int32_t N, int64_t T, int64_t ca
     const int64_t i = base + tid;
     int64_t nch = 0, nck = 0;
     if (i < N) {
-      const int64_t len = (int64_t)seq_bos[i + 1] - seq_bos[i];
+      const int64_t len = small ? (int64_t)sh_bos[i + 1] - sh_bos[i]
+                                : (int64_t)seq_bos[i + 1] - seq_bos[i];
       nch = (len + kChunk - 1) / kChunk;
       nck = ck_every > 0 ? len / ck_every : 0;
       if (sidx) {
@@ -110,6 +117,7 @@ chunk_index_kernel(const void *cu, int cu_type, int32_t N, int64_t T, int64_t ca
     if (i <= N) {
       const int64_t ex_c = c0 + inc_c - nch;
       cu_chunks[i] = (int32_t)ex_c;
+      if (small) sh_cc[i] = (int32_t)ex_c;
       if (ck_cs && ck_every > 0) {
         const int64_t ex_k = c1 + inc_k - nck;
         if (load_index(ck_cs, ck_cs_type, i) != ex_k)
@@ -122,7 +130,8 @@ chunk_index_kernel(const void *cu, int cu_type, int32_t N, int64_t T, int64_t ca
   __threadfence_block();
   __syncthreads();
 
-  int64_t total = cu_chunks[N];
+  const int32_t *cc = small ? sh_cc : cu_chunks;
+  int64_t total = cc[N];
   if (total > cap) {
     if (tid == 0) atomicOr(&sh_status, GDN_STATUS_CHUNK_CAPACITY);
     total = cap;
@@ -134,10 +143,10 @@ chunk_index_kernel(const void *cu, int cu_type, int32_t N, int64_t T, int64_t ca
       int lo = 0, hi = N - 1;  // largest i in [0, N-1] with cu_chunks[i] <= f
       while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
-        if (cu_chunks[mid] <= f) lo = mid; else hi = mid - 1;
+        if (cc[mid] <= f) lo = mid; else hi = mid - 1;
       }
       si = lo;
-      sc = (int32_t)(f - cu_chunks[lo]);
+      sc = (int32_t)(f - cc[lo]);
     }
     chunk_idx[2 * f] = si;
     chunk_idx[2 * f + 1] = sc;

@@ -8,7 +8,7 @@
 //
 //   A[t][j] = beta_t exp(G_t - G_j) (k_t . k_j)   for j < t, else 0
 //   T       = (I + A)^{-1}                          (unit lower triangular)
-//   W       = T diag(beta exp(G)) K,   U = T diag(beta) V
+//   W       = T diag(beta exp(G)) K,   U = T diag(beta) V   (W stored as -W)
 //   Ktilde  = diag(exp(G_last - G)) K
 //
 // so that the state pass can do N = U - W S and S' = exp(G_last) S +
@@ -28,15 +28,18 @@ namespace gdn {
 
 template <typename T> struct Pad { static constexpr int v = 16 / sizeof(T); };
 
+// LDS plan (about 53 KB for bf16 at D = 128, so three workgroups share a CU):
+// k rows are needed only for K K^T, v (transposed) only after it, so they
+// share storage; A is inverted in place into T; the two spare columns of the
+// padded A/T rows hold G and beta.
 template <typename T, int D>
 struct IntraSmem {
-  T Ks[64][D + Pad<T>::v];        // k rows (normalised), natural order
-  T KsT[D][64 + Pad<T>::v];       // the same, transposed
-  T VsT[D][64 + Pad<T>::v];       // v, transposed
-  float Am[64][64 + 4];
-  float Tm[64][64 + 4];
-  float Gs[64];
-  float Bs[64];
+  union {
+    T Ks[64][D + Pad<T>::v];      // k rows (normalised), natural order
+    T VsT[D][64 + Pad<T>::v];     // v, transposed
+  } kv;
+  T KsT[D][64 + Pad<T>::v];       // k (normalised), transposed
+  float AT[64][64 + 4];           // A, then T in place; [t][64] = G, [t][65] = beta
 };
 
 template <typename T, int D>
@@ -47,9 +50,9 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   IntraSmem<T, D> &sm = *reinterpret_cast<IntraSmem<T, D> *>(smem_raw);
 
-  const int64_t ch = blockIdx.x;
   const int H = a.H;
-  const int f = (int)(ch / H), h = (int)(ch % H);
+  const int f = (int)(blockIdx.x / H), h = (int)(blockIdx.x % H);
+  const int64_t ch = ws_index(f, h, a.cap);
   if (f >= a.n_chunks[0]) return;
   const int seq = a.chunk_idx[2 * f], cidx = a.chunk_idx[2 * f + 1];
   const int64_t bos = (int64_t)a.seq_bos[seq] + (int64_t)kChunk * cidx;
@@ -57,38 +60,31 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
+  float(*AT)[68] = sm.AT;
 
-  // ---- load k (normalised), v; gates ------------------------------------
+  // ---- load k (normalised) and v; gates ----------------------------------
+  const int lt = tid >> 2, lp = tid & 3;   // row and row part of this thread
+  float vx[D / 4];
   {
-    const int t = tid >> 2, p = tid & 3;
-    const bool valid = t < len;
+    const bool valid = lt < len;
     const int kh = h / (H / a.hk), vh = h / (H / a.hv);
     float x[D / 4];
     if (valid) {
-      const T *row = (const T *)a.k + ((bos + t) * a.hk + kh) * D;
-      load_row_part<T, D>(row, p, x);
+      load_row_part<T, D>((const T *)a.k + ((bos + lt) * a.hk + kh) * D, lp, x);
+      load_row_part<T, D>((const T *)a.v + ((bos + lt) * a.hv + vh) * D, lp, vx);
     } else {
 #pragma unroll
-      for (int e = 0; e < D / 4; ++e) x[e] = 0.f;
+      for (int e = 0; e < D / 4; ++e) x[e] = vx[e] = 0.f;
     }
     float inv = 1.f;
     if (a.l2norm) inv = row_inv_norm<D>(x);
 #pragma unroll
     for (int e = 0; e < D / 4; ++e) {
-      const int col = row_part_idx(p, e);
+      const int col = row_part_idx(lp, e);
       const T val = from_f32<T>(x[e] * inv);
-      sm.Ks[t][col] = val;
-      sm.KsT[col][t] = val;
+      sm.kv.Ks[lt][col] = val;
+      sm.KsT[col][lt] = val;
     }
-    if (valid) {
-      const T *row = (const T *)a.v + ((bos + t) * a.hv + vh) * D;
-      load_row_part<T, D>(row, p, x);
-    } else {
-#pragma unroll
-      for (int e = 0; e < D / 4; ++e) x[e] = 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < D / 4; ++e) sm.VsT[row_part_idx(p, e)][t] = from_f32<T>(x[e]);
   }
   if (wave == 0) {
     const int t = lane;
@@ -104,8 +100,8 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
       const float y = __shfl_up(la, o);
       if (lane >= o) la += y;
     }
-    sm.Gs[t] = la;
-    sm.Bs[t] = be;
+    AT[t][64] = la;
+    AT[t][65] = be;
     a.Gw[ch * kChunk + t] = la;
   }
   __syncthreads();
@@ -113,28 +109,42 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
   // ---- A = strictly-lower(beta_t exp(G_t - G_j) k_t.k_j) ------------------
   {
     const int it = wave;
+    f32x4 acc[4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (jt <= it) {
 #pragma unroll
         for (int kt = 0; kt < KS_D; ++kt) {
           const int k0 = kt * 4 * KPL + g * KPL;
-          const typename M::frag fa = *reinterpret_cast<const typename M::frag *>(&sm.Ks[16 * it + c][k0]);
-          const typename M::frag fb = *reinterpret_cast<const typename M::frag *>(&sm.Ks[16 * jt + c][k0]);
-          acc = M::mma(fa, fb, acc);
+          const typename M::frag fa = *reinterpret_cast<const typename M::frag *>(&sm.kv.Ks[16 * it + c][k0]);
+          const typename M::frag fb = *reinterpret_cast<const typename M::frag *>(&sm.kv.Ks[16 * jt + c][k0]);
+          acc[jt] = M::mma(fa, fb, acc[jt]);
         }
       }
+    }
+    float Gt[4], Bt[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      Gt[r] = AT[16 * it + 4 * g + r][64];
+      Bt[r] = AT[16 * it + 4 * g + r][65];
+    }
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      const int j = 16 * jt + c;
+      const float Gj = AT[j][64];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * it + 4 * g + r, j = 16 * jt + c;
-        sm.Am[t][j] = (j < t) ? sm.Bs[t] * gexp(sm.Gs[t] - sm.Gs[j]) * acc[r] : 0.f;
+        const int t = 16 * it + 4 * g + r;
+        AT[t][j] = (j < t) ? Bt[r] * gexp(Gt[r] - Gj) * acc[jt][r] : 0.f;
       }
     }
   }
   __syncthreads();
 
-  // ---- T = (I + A)^{-1}: diagonal blocks --------------------------------
+  // ---- v into LDS (transposed, over the k rows); T diagonal blocks -------
+#pragma unroll
+  for (int e = 0; e < D / 4; ++e) sm.kv.VsT[row_part_idx(lp, e)][lt] = from_f32<T>(vx[e]);
   {
     const int bw = wave;
     float tc[16];
@@ -142,17 +152,13 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
     for (int i = 0; i < 16; ++i) {
       float s = (i == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < i; ++m) s = fmaf(-sm.Am[16 * bw + i][16 * bw + m], tc[m], s);
+      for (int m = 0; m < i; ++m) s = fmaf(-AT[16 * bw + i][16 * bw + m], tc[m], s);
       tc[i] = (i < c) ? 0.f : s;
     }
+    // every lane has read its A block: overwrite it with T (upper part 0)
     if (g == 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm.Tm[16 * bw + i][16 * bw + c] = tc[i];
-    }
-    // zero the blocks above the diagonal
-    for (int e = lane; e < 16 * 64; e += 64) {
-      const int i = e >> 6, j = e & 63;
-      if (j >= 16 * (bw + 1)) sm.Tm[16 * bw + i][j] = 0.f;
+      for (int i = 0; i < 16; ++i) AT[16 * bw + i][16 * bw + c] = tc[i];
     }
   }
   __syncthreads();
@@ -160,26 +166,26 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
 #pragma unroll
   for (int bi = 1; bi < 4; ++bi) {
     const int bj = wave;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
     if (bj < bi) {
+      // X = sum_m A_{bi,m} T_{m,bj}; row block bi still holds A
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
       for (int m = bj; m < bi; ++m) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const float fa = sm.Am[16 * bi + c][16 * m + 4 * kt + g];
-          const float fb = sm.Tm[16 * m + 4 * kt + g][16 * bj + c];
-          x = Mfma<float>::mma(fa, fb, x);
-        }
+        for (int kt = 0; kt < 4; ++kt)
+          x = Mfma<float>::mma(AT[16 * bi + c][16 * m + 4 * kt + g],
+                               AT[16 * m + 4 * kt + g][16 * bj + c], x);
       }
       // T_ij = -T_ii X; X rows 4g..4g+3 sit in this lane group: contract over
       // them in pi order (slot kt of group g is row 4g + kt).
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const float fa = sm.Tm[16 * bi + c][16 * bi + 4 * g + kt];
-        y = Mfma<float>::mma(fa, x[kt], y);
-      }
+      for (int kt = 0; kt < 4; ++kt)
+        y = Mfma<float>::mma(AT[16 * bi + c][16 * bi + 4 * g + kt], x[kt], y);
+    }
+    __syncthreads();  // all reads of row block bi's A are done
+    if (bj < bi) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.Tm[16 * bi + 4 * g + r][16 * bj + c] = -y[r];
+      for (int r = 0; r < 4; ++r) AT[16 * bi + 4 * g + r][16 * bj + c] = -y[r];
     }
     __syncthreads();
   }
@@ -193,7 +199,7 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
 #pragma unroll
       for (int e = 0; e < KPL; ++e) {
         const int j = kt * 4 * KPL + g * KPL + e;
-        M::set(bw[kt], e, sm.Tm[16 * w + c][j] * sm.Bs[j] * gexp(sm.Gs[j]));
+        M::set(bw[kt], e, AT[16 * w + c][j] * AT[j][65] * gexp(AT[j][64]));
       }
     }
     T *wf = (T *)a.Wf + ch * Ge::W_ELEMS + (int64_t)w * KS_D * 64 * KPL;
@@ -207,11 +213,12 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
             *reinterpret_cast<const typename M::frag *>(&sm.KsT[16 * dt + c][kt * 4 * KPL + g * KPL]);
         acc = M::mma(fa, bw[kt], acc);
       }
-      // lane holds W[16w + c][16dt + 4g + r] = slot s = 4dt + r
+      // lane holds W[16w + c][16dt + 4g + r] = slot s = 4dt + r; stored
+      // negated so the state pass accumulates U + (-W) S directly
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = 4 * dt + r;
-        M::set(out[s / KPL], s % KPL, acc[r]);
+        M::set(out[s / KPL], s % KPL, -acc[r]);
       }
     }
 #pragma unroll
@@ -226,7 +233,7 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
 #pragma unroll
       for (int e = 0; e < KPL; ++e) {
         const int j = kt * 4 * KPL + g * KPL + e;
-        M::set(au[kt], e, sm.Tm[16 * w + c][j] * sm.Bs[j]);
+        M::set(au[kt], e, AT[16 * w + c][j] * AT[j][65]);
       }
     }
     T *uf = (T *)a.Uf + ch * Ge::W_ELEMS;
@@ -236,7 +243,7 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
 #pragma unroll
       for (int kt = 0; kt < KS_C; ++kt) {
         const typename M::frag fb =
-            *reinterpret_cast<const typename M::frag *>(&sm.VsT[16 * jv + c][kt * 4 * KPL + g * KPL]);
+            *reinterpret_cast<const typename M::frag *>(&sm.kv.VsT[16 * jv + c][kt * 4 * KPL + g * KPL]);
         acc = M::mma(au[kt], fb, acc);
       }
       T *dst = uf + (((int64_t)jv * 4 + w) * 64 + lane) * 4;
@@ -246,7 +253,7 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
   }
   // ---- Ktilde^T fragments ---------------------------------------------------
   {
-    const float glast = sm.Gs[63];
+    const float glast = AT[63][64];
     T *kf = (T *)a.Kf + ch * Ge::W_ELEMS;
     constexpr int NFRAG = NT * KS_C * 64;
     for (int fi = tid; fi < NFRAG; fi += 256) {
@@ -256,7 +263,7 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
 #pragma unroll
       for (int e = 0; e < KPL; ++e) {
         const int j = pi_idx(fg, kt * KPL + e);
-        M::set(v, e, to_f32(sm.KsT[16 * it2 + fc][j]) * gexp(glast - sm.Gs[j]));
+        M::set(v, e, to_f32(sm.KsT[16 * it2 + fc][j]) * gexp(glast - AT[j][64]));
       }
       *reinterpret_cast<typename M::frag *>(kf + (int64_t)fi * KPL) = v;
     }
