@@ -27,6 +27,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -301,11 +303,10 @@ def main():
     for i in range(max(args.warmup, 1)):
         call((ctypes.c_void_p * 5)(*ev[i]))
     torch.cuda.synchronize()
-    phase_ms = {ph: 0.0 for ph in PHASES}
-    for i in range(max(args.warmup, 1)):
-        for j, ph in enumerate(PHASES):
-            phase_ms[ph] += elapsed_ms(L, ev[i][j], ev[i][j + 1])
-    phase_ms = {ph: v / max(args.warmup, 1) for ph, v in phase_ms.items()}
+    # median over the warm-up calls after the first (which pays one-time set-up)
+    used = ev[1:] if len(ev) > 1 else ev
+    phase_ms = {ph: float(np.median([elapsed_ms(L, e[j], e[j + 1]) for e in used]))
+                for j, ph in enumerate(PHASES)}
     dom = max(PHASES, key=lambda ph: phase_ms[ph])
     di = PHASES.index(dom)
 

@@ -77,6 +77,35 @@ template <> struct Mfma<float> {
   static __device__ __forceinline__ frag pack(const float *x) { return x[0]; }
 };
 
+// ---------------------------------------------------------------------------
+// Transposed LDS reads (ds_read_b64_tr_b16).  For a row-major bf16 matrix X in
+// LDS, lane l = 16g + c passing the address of
+//     X[r0(g) + c / 4][col0 + 4 (c % 4)]
+// receives X[r0(g) + e][col0 + c] for e = 0..3: four consecutive rows of one
+// column.  (Within each 16-lane group, result element e of lane c is element
+// c % 4 of the 8 bytes that lane 4e + c / 4 addressed.)  Two such reads give
+// the eight-row operand run of a bf16 matrix-core fragment, so matrices can
+// stay row-major in LDS and still feed products that contract over rows.
+// ---------------------------------------------------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i16x4 lds_read_tr4(const bf16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4 *)(p));
+}
+
+// Rows r0(g) .. r0(g) + 3 and r1(g) .. r1(g) + 3 of column col0 + c of a
+// row-major LDS matrix with leading dimension ld, as one bf16x8 fragment.
+__device__ __forceinline__ bf16x8 lds_col_frag(const bf16 *X, int ld, int r0, int r1,
+                                               int col0, int c) {
+  const int rr = c >> 2, cc = col0 + 4 * (c & 3);
+  const i16x4 lo = lds_read_tr4(X + (r0 + rr) * ld + cc);
+  const i16x4 hi = lds_read_tr4(X + (r1 + rr) * ld + cc);
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Contraction index of slot s in lane group g (see the header comment).
 __device__ __forceinline__ int pi_idx(int g, int s) {
   return 16 * (s >> 2) + 4 * g + (s & 3);

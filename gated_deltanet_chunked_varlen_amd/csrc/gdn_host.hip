@@ -35,7 +35,7 @@ bool valid_state_dtype(int d) { return d == GDN_F32 || d == GDN_BF16 || d == GDN
 bool valid_itype(int t) { return t == GDN_I32 || t == GDN_I64; }
 
 struct Layout {
-  size_t chunk_idx, cu_chunks, seq_bos, n_chunks, Wf, Kf, Uf, Hf, Nf, Gw, total;
+  size_t chunk_idx, chunk_tok, cu_chunks, seq_bos, n_chunks, Wf, Kf, Uf, Hf, Nf, Gw, total;
 };
 
 Layout plan(const gdn_prefill_params *p) {
@@ -47,6 +47,7 @@ Layout plan(const gdn_prefill_params *p) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
   L.chunk_idx = take(sizeof(int32_t) * 2 * (size_t)std::max<int64_t>(cap, 1));
+  L.chunk_tok = take(sizeof(int32_t) * 2 * (size_t)std::max<int64_t>(cap, 1));
   L.cu_chunks = take(sizeof(int32_t) * (size_t)(N + 1));
   L.seq_bos = take(sizeof(int32_t) * (size_t)(N + 1));
   L.n_chunks = take(sizeof(int32_t));
@@ -214,7 +215,7 @@ int gdn_build_chunk_indices(const void *cu_seqlens, int32_t cu_type, int32_t num
   if (rc != GDN_OK) return rc;
   hipError_t e = launch_chunk_index(cu_seqlens, cu_type, num_seqs, total_tokens, cap,
                                     chunk_indices, cu_chunks, seq_starts, n_chunks, status,
-                                    nullptr, 0, 0, nullptr, 0, 0, (hipStream_t)stream);
+                                    nullptr, 0, 0, nullptr, 0, 0, nullptr, (hipStream_t)stream);
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
@@ -247,6 +248,7 @@ static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *
   a.l2norm = p->use_qk_l2norm_in_kernel ? 1 : 0;
   a.out = p->output;
   a.chunk_idx = (int32_t *)(ws + L.chunk_idx);
+  a.chunk_tok = (int32_t *)(ws + L.chunk_tok);
   a.cu_chunks = (int32_t *)(ws + L.cu_chunks);
   a.seq_bos = (int32_t *)(ws + L.seq_bos);
   a.n_chunks = (int32_t *)(ws + L.n_chunks);
@@ -289,7 +291,7 @@ static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *
     e = launch_chunk_index(p->cu_seqlens, p->cu_seqlens_type, a.N, a.T, a.cap, a.chunk_idx,
                            a.cu_chunks, a.seq_bos, a.n_chunks, a.status,
                            a.ck_every > 0 ? a.ck_cs : nullptr, a.ck_cs_type, a.ck_every,
-                           a.sidx, a.sidx_type, a.pool_rows, s);
+                           a.sidx, a.sidx_type, a.pool_rows, a.chunk_tok, s);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess && a.cap > 0) e = launch_intra(a, s);
   if (e == hipSuccess) e = mark(2);

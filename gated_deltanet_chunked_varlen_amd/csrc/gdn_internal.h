@@ -22,6 +22,7 @@ struct Args {
   int32_t *cu_chunks;  // [N+1]
   int32_t *seq_bos;    // [N+1] sanitised sequence starts
   int32_t *n_chunks;   // [1]
+  int32_t *chunk_tok;  // [cap][2] first token, length (0 for unused slots)
   int64_t cap;
   // intermediates
   void *Wf, *Kf, *Uf, *Hf, *Nf;
@@ -56,7 +57,7 @@ hipError_t launch_chunk_index(const void *cu, int cu_type, int32_t N, int64_t T,
                               int32_t *seq_bos, int32_t *n_chunks, int32_t *status,
                               const void *ck_cs, int ck_cs_type, int32_t ck_every,
                               const void *sidx, int sidx_type, int64_t pool_rows,
-                              hipStream_t s);
+                              int32_t *chunk_tok, hipStream_t s);
 hipError_t launch_intra(const Args &a, hipStream_t s);
 hipError_t launch_state(const Args &a, hipStream_t s);
 hipError_t launch_output(const Args &a, hipStream_t s);

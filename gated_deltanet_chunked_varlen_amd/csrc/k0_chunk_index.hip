@@ -12,7 +12,9 @@
 //   pass 2  n_i = ceil(len_i / 64), cu_chunks = exclusive scan; checkpoint
 //           starts are recomputed and compared when given; state indices are
 //           range-checked;
-//   pass 3  every table slot f < cap: binary search of cu_chunks.
+//   pass 3  every table slot f < cap: binary search of cu_chunks; beside the
+//           (sequence, chunk) table, an optional (first token, length) table
+//           that lets a chunk's workgroup find its rows with one load.
 // Scans run tile by tile (1024 sequences per tile) with a carried prefix.
 #include "gdn_common.h"
 #include "gdn_internal.h"
@@ -61,7 +63,7 @@ chunk_index_kernel(const void *cu, int cu_type, int32_t N, int64_t T, int64_t ca
                    int32_t *chunk_idx, int32_t *cu_chunks, int32_t *seq_bos,
                    int32_t *n_chunks, int32_t *status, const void *ck_cs,
                    int ck_cs_type, int32_t ck_every, const void *sidx,
-                   int sidx_type, int64_t pool_rows) {
+                   int sidx_type, int64_t pool_rows, int32_t *chunk_tok) {
   __shared__ int64_t sh_wave[kK0Threads / 64];
   __shared__ int64_t sh_carry[2];
   __shared__ unsigned sh_status;
@@ -138,7 +140,7 @@ chunk_index_kernel(const void *cu, int cu_type, int32_t N, int64_t T, int64_t ca
   }
   // pass 3: table entries
   for (int64_t f = tid; f < cap; f += kK0Threads) {
-    int32_t si = -1, sc = -1;
+    int32_t si = -1, sc = -1, tb = 0, tl = 0;
     if (f < total) {
       int lo = 0, hi = N - 1;  // largest i in [0, N-1] with cu_chunks[i] <= f
       while (lo < hi) {
@@ -147,9 +149,17 @@ chunk_index_kernel(const void *cu, int cu_type, int32_t N, int64_t T, int64_t ca
       }
       si = lo;
       sc = (int32_t)(f - cc[lo]);
+      const int32_t b0 = small ? sh_bos[lo] : seq_bos[lo];
+      const int32_t b1 = small ? sh_bos[lo + 1] : seq_bos[lo + 1];
+      tb = b0 + kChunk * sc;
+      tl = min(kChunk, b1 - tb);
     }
     chunk_idx[2 * f] = si;
     chunk_idx[2 * f + 1] = sc;
+    if (chunk_tok) {
+      chunk_tok[2 * f] = tb;
+      chunk_tok[2 * f + 1] = tl;
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -163,10 +173,10 @@ hipError_t launch_chunk_index(const void *cu, int cu_type, int32_t N, int64_t T,
                               int32_t *seq_bos, int32_t *n_chunks, int32_t *status,
                               const void *ck_cs, int ck_cs_type, int32_t ck_every,
                               const void *sidx, int sidx_type, int64_t pool_rows,
-                              hipStream_t s) {
+                              int32_t *chunk_tok, hipStream_t s) {
   hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(kK0Threads), 0, s, cu, cu_type,
                      N, T, cap, chunk_idx, cu_chunks, seq_bos, n_chunks, status, ck_cs,
-                     ck_cs_type, ck_every, sidx, sidx_type, pool_rows);
+                     ck_cs_type, ck_every, sidx, sidx_type, pool_rows, chunk_tok);
   return hipGetLastError();
 }
 

@@ -286,11 +286,283 @@ static hipError_t launch_intra_t(const Args &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// bf16 variant.  k and v stay row-major in LDS and every product that
+// contracts over the chunk's rows reads them through transposed LDS reads
+// (lds_col_frag), so there is no transposed copy: one padded 64 x D bf16
+// buffer holds the normalised k rows and, once W and Ktilde^T are out, the v
+// rows.  With the fp32 A/T buffer that is about 35 KB at D = 128, and four
+// workgroups share a CU.  The chunk's first token and length come from the
+// (first token, length) table in one load.
+// ---------------------------------------------------------------------------
+template <int D>
+struct IntraSmemB {
+  static constexpr int LDK = D + 16;  // row pitch in elements (32 B pad)
+  bf16 KV[64][LDK];                   // normalised k rows, later v rows
+  float AT[64][68];                   // A, then T; [t][64] = G, [t][65] = beta
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) intra_kernel_bf16(Args a) {
+  using M = Mfma<bf16>;
+  typedef bf16x8 frag;
+  constexpr int NT = D / 16, KS_D = D / 32, KS_C = 2, NV = D / 32;
+  constexpr int LDK = IntraSmemB<D>::LDK;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  IntraSmemB<D> &sm = *reinterpret_cast<IntraSmemB<D> *>(smem_raw);
+
+  const int H = a.H;
+  const int f = (int)(blockIdx.x / H), h = (int)(blockIdx.x % H);
+  const int tb = a.chunk_tok[2 * f], len = a.chunk_tok[2 * f + 1];
+  if (len <= 0) return;
+  const int64_t bos = tb;
+  const int64_t ch = ws_index(f, h, a.cap);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  float(*AT)[68] = sm.AT;
+  bf16(*KV)[LDK] = sm.KV;
+
+  // ---- k (normalised) into LDS, v kept in registers; gates ---------------
+  const int lt = tid >> 2, lp = tid & 3;  // row and row part of this thread
+  u32x4 vraw[NV];
+  {
+    const bool valid = lt < len;
+    const int kh = h / (H / a.hk), vh = h / (H / a.hv);
+    u32x4 kraw[NV];
+    const bf16 *krow = (const bf16 *)a.k + ((bos + lt) * a.hk + kh) * D;
+    const bf16 *vrow = (const bf16 *)a.v + ((bos + lt) * a.hv + vh) * D;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      kraw[i] = valid ? *reinterpret_cast<const u32x4 *>(krow + 32 * i + 8 * lp) : u32x4{0, 0, 0, 0};
+      vraw[i] = valid ? *reinterpret_cast<const u32x4 *>(vrow + 32 * i + 8 * lp) : u32x4{0, 0, 0, 0};
+    }
+    float x[D / 4];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bf16x8 kv8 = __builtin_bit_cast(bf16x8, kraw[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[8 * i + e] = (float)kv8[e];
+    }
+    float inv = 1.f;
+    if (a.l2norm) inv = row_inv_norm<D>(x);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = x[8 * i + e] * inv;
+      *reinterpret_cast<frag *>(&KV[lt][32 * i + 8 * lp]) = M::pack(y);
+    }
+  }
+  if (wave == 0) {
+    const int t = lane;
+    const bool valid = t < len;
+    float la = 0.f, be = 0.f;
+    if (valid) {
+      const int64_t gi = (bos + t) * H + h;
+      la = a.g ? logf(a.g[gi]) : 0.f;
+      be = a.beta ? a.beta[gi] : 1.f;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(la, o);
+      if (lane >= o) la += y;
+    }
+    AT[t][64] = la;
+    AT[t][65] = be;
+    a.Gw[ch * kChunk + t] = la;
+  }
+  __syncthreads();
+
+  // ---- A = strictly-lower(beta_t exp(G_t - G_j) k_t.k_j) ------------------
+  {
+    const int it = wave;
+    f32x4 acc[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (jt <= it) {
+#pragma unroll
+        for (int kt = 0; kt < KS_D; ++kt) {
+          const int k0 = kt * 32 + g * 8;
+          const frag fa = *reinterpret_cast<const frag *>(&KV[16 * it + c][k0]);
+          const frag fb = *reinterpret_cast<const frag *>(&KV[16 * jt + c][k0]);
+          acc[jt] = M::mma(fa, fb, acc[jt]);
+        }
+      }
+    }
+    float Gt[4], Bt[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      Gt[r] = AT[16 * it + 4 * g + r][64];
+      Bt[r] = AT[16 * it + 4 * g + r][65];
+    }
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      const int j = 16 * jt + c;
+      const float Gj = AT[j][64];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * it + 4 * g + r;
+        AT[t][j] = (j < t) ? Bt[r] * gexp(Gt[r] - Gj) * acc[jt][r] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- T diagonal blocks (forward substitution, lane c = column c) --------
+  {
+    const int bw = wave;
+    float tc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = (i == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) s = fmaf(-AT[16 * bw + i][16 * bw + m], tc[m], s);
+      tc[i] = (i < c) ? 0.f : s;
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) AT[16 * bw + i][16 * bw + c] = tc[i];
+    }
+  }
+  __syncthreads();
+  // ---- off-diagonal blocks, one row block at a time ----------------------
+#pragma unroll
+  for (int bi = 1; bi < 4; ++bi) {
+    const int bj = wave;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    if (bj < bi) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      for (int m = bj; m < bi; ++m) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          x = Mfma<float>::mma(AT[16 * bi + c][16 * m + 4 * kt + g],
+                               AT[16 * m + 4 * kt + g][16 * bj + c], x);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        y = Mfma<float>::mma(AT[16 * bi + c][16 * bi + 4 * g + kt], x[kt], y);
+    }
+    __syncthreads();
+    if (bj < bi) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) AT[16 * bi + 4 * g + r][16 * bj + c] = -y[r];
+    }
+    __syncthreads();
+  }
+
+  const int w = wave;  // token tile of this wave
+  // ---- W (as W^T tiles): A operand = k columns via transposed reads --------
+  {
+    frag bw[KS_C];
+#pragma unroll
+    for (int kt = 0; kt < KS_C; ++kt) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = kt * 32 + g * 8 + e;
+        y[e] = AT[16 * w + c][j] * AT[j][65] * gexp(AT[j][64]);
+      }
+      bw[kt] = M::pack(y);
+    }
+    bf16 *wf = (bf16 *)a.Wf + ch * (int64_t)(64 * D) + (int64_t)w * KS_D * 64 * 8;
+    frag out[KS_D];
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < KS_C; ++kt) {
+        const frag fa = lds_col_frag(&KV[0][0], LDK, kt * 32 + g * 8, kt * 32 + g * 8 + 4, 16 * dt, c);
+        acc = M::mma(fa, bw[kt], acc);
+      }
+      // lane holds W[16w + c][16dt + 4g + r] = slot s = 4dt + r; stored
+      // negated so the state pass accumulates U + (-W) S directly
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = 4 * dt + r;
+        out[s / 8][s % 8] = (bf16)(-acc[r]);
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < KS_D; ++kt)
+      *reinterpret_cast<frag *>(wf + ((int64_t)kt * 64 + lane) * 8) = out[kt];
+  }
+  // ---- Ktilde^T fragments: rows pi(g, 8kt + e) of k column 16 it2 + c ------
+  {
+    const float glast = AT[63][64];
+    bf16 *kf = (bf16 *)a.Kf + ch * (int64_t)(64 * D);
+#pragma unroll
+    for (int q = 0; q < NT * KS_C / 4; ++q) {
+      const int fidx = wave + 4 * q;  // fragment block (row tile it2, k-step kt)
+      const int kt = fidx % KS_C, it2 = fidx / KS_C;
+      const int r0 = 32 * kt + 4 * g, r1 = r0 + 16;
+      const frag kv = lds_col_frag(&KV[0][0], LDK, r0, r1, 16 * it2, c);
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = (e < 4 ? r0 : r1) + (e & 3);
+        y[e] = (float)kv[e] * gexp(glast - AT[j][64]);
+      }
+      *reinterpret_cast<frag *>(kf + ((int64_t)fidx * 64 + lane) * 8) = M::pack(y);
+    }
+  }
+  __syncthreads();  // k rows consumed
+#pragma unroll
+  for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4 *>(&KV[lt][32 * i + 8 * lp]) = vraw[i];
+  __syncthreads();
+  // ---- U ------------------------------------------------------------------
+  {
+    frag au[KS_C];
+#pragma unroll
+    for (int kt = 0; kt < KS_C; ++kt) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = kt * 32 + g * 8 + e;
+        y[e] = AT[16 * w + c][j] * AT[j][65];
+      }
+      au[kt] = M::pack(y);
+    }
+    bf16 *uf = (bf16 *)a.Uf + ch * (int64_t)(64 * D);
+#pragma unroll
+    for (int jv = 0; jv < NT; ++jv) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < KS_C; ++kt) {
+        const frag fb = lds_col_frag(&KV[0][0], LDK, kt * 32 + g * 8, kt * 32 + g * 8 + 4, 16 * jv, c);
+        acc = M::mma(au[kt], fb, acc);
+      }
+      bf16 *dst = uf + (((int64_t)jv * 4 + w) * 64 + lane) * 4;
+      bf16x4 o4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o4[r] = (bf16)acc[r];
+      *reinterpret_cast<bf16x4 *>(dst) = o4;
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_intra_bf16(const Args &a, hipStream_t s) {
+  const size_t smem = sizeof(IntraSmemB<D>);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)intra_kernel_bf16<D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t blocks = a.cap * a.H;
+  if (blocks == 0) return hipSuccess;
+  intra_kernel_bf16<D><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_intra(const Args &a, hipStream_t s) {
   if (a.dtype == GDN_BF16) {
-    if (a.D == 128) return launch_intra_t<bf16, 128>(a, s);
-    if (a.D == 64) return launch_intra_t<bf16, 64>(a, s);
-    return launch_intra_t<bf16, 32>(a, s);
+    if (a.D == 128) return launch_intra_bf16<128>(a, s);
+    if (a.D == 64) return launch_intra_bf16<64>(a, s);
+    return launch_intra_bf16<32>(a, s);
   }
   if (a.D == 128) return launch_intra_t<float, 128>(a, s);
   if (a.D == 64) return launch_intra_t<float, 64>(a, s);
