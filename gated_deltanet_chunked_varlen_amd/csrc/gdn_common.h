@@ -106,6 +106,17 @@ __device__ __forceinline__ bf16x8 lds_col_frag(const bf16 *X, int ld, int r0, in
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every outstanding global load and store of the calling wave; this
+// one waits for the wave's LDS accesses alone, so global loads issued ahead of
+// time stay in flight across it.  Use it where the waves of a workgroup
+// exchange data through LDS only.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Contraction index of slot s in lane group g (see the header comment).
 __device__ __forceinline__ int pi_idx(int g, int s) {
   return 16 * (s >> 2) + 4 * g + (s & 3);
@@ -166,6 +177,40 @@ __device__ __forceinline__ void load_row_part(const Tin *row, int p, float (&x)[
     const Tin *src = row + 32 * (i >> 3) + 8 * p;
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[i + e] = to_f32(src[e]);
+  }
+}
+
+// bf16 row part of lane part p (the runs of load_row_part), optionally
+// normalised with row_inv_norm, rounded back to bf16: NV = D / 32 fragments
+// of 8 elements, fragment i holding row elements 32 i + 8 p .. + 7.  The
+// intra-chunk and output passes both use this, so they see the same k rows.
+template <int D>
+__device__ __forceinline__ void load_norm_row_bf16(const bf16 *row, int p, bool valid,
+                                                   bool l2norm, bf16x8 (&out)[D / 32]) {
+  constexpr int NV = D / 32;
+  u32x4 raw[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    raw[i] = valid ? *reinterpret_cast<const u32x4 *>(row + 32 * i + 8 * p) : u32x4{0, 0, 0, 0};
+  if (!l2norm) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) out[i] = __builtin_bit_cast(bf16x8, raw[i]);
+    return;
+  }
+  float x[D / 4];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const bf16x8 r8 = __builtin_bit_cast(bf16x8, raw[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[8 * i + e] = (float)r8[e];
+  }
+  const float inv = row_inv_norm<D>(x);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const f32x8 y = {x[8 * i] * inv,     x[8 * i + 1] * inv, x[8 * i + 2] * inv,
+                     x[8 * i + 3] * inv, x[8 * i + 4] * inv, x[8 * i + 5] * inv,
+                     x[8 * i + 6] * inv, x[8 * i + 7] * inv};
+    out[i] = __builtin_convertvector(y, bf16x8);
   }
 }
 

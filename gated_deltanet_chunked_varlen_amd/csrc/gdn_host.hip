@@ -87,15 +87,18 @@ void fill_strides(const int64_t in[4], int64_t H, int64_t D, int64_t out[4]) {
   }
 }
 
-int check_device() {
+// Checks that the current device is a gfx950 and reports its CU count
+// (cached per device).
+int check_device(int *num_cus = nullptr) {
   static std::mutex mu;
   static int cached[64];
+  static int cus[64];
   static bool init = false;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GDN_ERR_DEVICE;
   std::lock_guard<std::mutex> lock(mu);
   if (!init) {
-    for (int i = 0; i < 64; ++i) cached[i] = 0;
+    for (int i = 0; i < 64; ++i) cached[i] = cus[i] = 0;
     init = true;
   }
   if (dev < 0 || dev >= 64) return GDN_ERR_DEVICE;
@@ -103,7 +106,9 @@ int check_device() {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GDN_ERR_DEVICE;
     cached[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    cus[dev] = prop.multiProcessorCount;
   }
+  if (num_cus) *num_cus = cus[dev];
   return cached[dev] == 1 ? GDN_OK : GDN_ERR_DEVICE;
 }
 
@@ -222,7 +227,8 @@ int gdn_build_chunk_indices(const void *cu_seqlens, int32_t cu_type, int32_t num
 static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *events) {
   int rc = gdn_validate_host(p);
   if (rc != GDN_OK) return rc;
-  rc = check_device();
+  int num_cus = 0;
+  rc = check_device(&num_cus);
   if (rc != GDN_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
   const Layout L = plan(p);
@@ -280,6 +286,7 @@ static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *
   a.ck_cs = p->checkpoint_cu_starts;
   a.ck_cs_type = p->checkpoint_cu_starts_type;
   a.status = p->status;
+  a.num_cus = num_cus;
   if (a.ck_every > 0 && !a.ck) a.ck_every = 0;
 
   auto mark = [&](int i) -> hipError_t {

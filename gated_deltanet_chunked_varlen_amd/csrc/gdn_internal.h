@@ -49,6 +49,7 @@ struct Args {
   // validation
   int64_t pool_rows;  // rows addressable through state_indices
   int32_t *status;
+  int32_t num_cus;    // compute units of the device (launch shapes)
 };
 
 // Chunk-index builder: one workgroup.

@@ -104,7 +104,7 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
     AT[t][65] = be;
     a.Gw[ch * kChunk + t] = la;
   }
-  __syncthreads();
+  lds_sync();
 
   // ---- A = strictly-lower(beta_t exp(G_t - G_j) k_t.k_j) ------------------
   {
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
       }
     }
   }
-  __syncthreads();
+  lds_sync();
 
   // ---- v into LDS (transposed, over the k rows); T diagonal blocks -------
 #pragma unroll
@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
       for (int i = 0; i < 16; ++i) AT[16 * bw + i][16 * bw + c] = tc[i];
     }
   }
-  __syncthreads();
+  lds_sync();
   // ---- off-diagonal blocks, one row block at a time ----------------------
 #pragma unroll
   for (int bi = 1; bi < 4; ++bi) {
@@ -182,12 +182,12 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
       for (int kt = 0; kt < 4; ++kt)
         y = Mfma<float>::mma(AT[16 * bi + c][16 * bi + 4 * g + kt], x[kt], y);
     }
-    __syncthreads();  // all reads of row block bi's A are done
+    lds_sync();  // all reads of row block bi's A are done
     if (bj < bi) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) AT[16 * bi + 4 * g + r][16 * bj + c] = -y[r];
     }
-    __syncthreads();
+    lds_sync();
   }
 
   // ---- W (as W^T tiles) -------------------------------------------------
@@ -329,30 +329,15 @@ __global__ void __launch_bounds__(256) intra_kernel_bf16(Args a) {
   {
     const bool valid = lt < len;
     const int kh = h / (H / a.hk), vh = h / (H / a.hv);
-    u32x4 kraw[NV];
-    const bf16 *krow = (const bf16 *)a.k + ((bos + lt) * a.hk + kh) * D;
     const bf16 *vrow = (const bf16 *)a.v + ((bos + lt) * a.hv + vh) * D;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      kraw[i] = valid ? *reinterpret_cast<const u32x4 *>(krow + 32 * i + 8 * lp) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < NV; ++i)
       vraw[i] = valid ? *reinterpret_cast<const u32x4 *>(vrow + 32 * i + 8 * lp) : u32x4{0, 0, 0, 0};
-    }
-    float x[D / 4];
+    frag kn[NV];
+    load_norm_row_bf16<D>((const bf16 *)a.k + ((bos + lt) * a.hk + kh) * D, lp, valid,
+                          a.l2norm != 0, kn);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const bf16x8 kv8 = __builtin_bit_cast(bf16x8, kraw[i]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[8 * i + e] = (float)kv8[e];
-    }
-    float inv = 1.f;
-    if (a.l2norm) inv = row_inv_norm<D>(x);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      float y[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = x[8 * i + e] * inv;
-      *reinterpret_cast<frag *>(&KV[lt][32 * i + 8 * lp]) = M::pack(y);
-    }
+    for (int i = 0; i < NV; ++i) *reinterpret_cast<frag *>(&KV[lt][32 * i + 8 * lp]) = kn[i];
   }
   if (wave == 0) {
     const int t = lane;
@@ -372,7 +357,7 @@ __global__ void __launch_bounds__(256) intra_kernel_bf16(Args a) {
     AT[t][65] = be;
     a.Gw[ch * kChunk + t] = la;
   }
-  __syncthreads();
+  lds_sync();
 
   // ---- A = strictly-lower(beta_t exp(G_t - G_j) k_t.k_j) ------------------
   {
@@ -408,7 +393,7 @@ __global__ void __launch_bounds__(256) intra_kernel_bf16(Args a) {
       }
     }
   }
-  __syncthreads();
+  lds_sync();
 
   // ---- T diagonal blocks (forward substitution, lane c = column c) --------
   {
@@ -426,7 +411,7 @@ __global__ void __launch_bounds__(256) intra_kernel_bf16(Args a) {
       for (int i = 0; i < 16; ++i) AT[16 * bw + i][16 * bw + c] = tc[i];
     }
   }
-  __syncthreads();
+  lds_sync();
   // ---- off-diagonal blocks, one row block at a time ----------------------
 #pragma unroll
   for (int bi = 1; bi < 4; ++bi) {
@@ -444,12 +429,12 @@ __global__ void __launch_bounds__(256) intra_kernel_bf16(Args a) {
       for (int kt = 0; kt < 4; ++kt)
         y = Mfma<float>::mma(AT[16 * bi + c][16 * bi + 4 * g + kt], x[kt], y);
     }
-    __syncthreads();
+    lds_sync();
     if (bj < bi) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) AT[16 * bi + 4 * g + r][16 * bj + c] = -y[r];
     }
-    __syncthreads();
+    lds_sync();
   }
 
   const int w = wave;  // token tile of this wave
@@ -507,10 +492,10 @@ __global__ void __launch_bounds__(256) intra_kernel_bf16(Args a) {
       *reinterpret_cast<frag *>(kf + ((int64_t)fidx * 64 + lane) * 8) = M::pack(y);
     }
   }
-  __syncthreads();  // k rows consumed
+  lds_sync();  // k rows consumed
 #pragma unroll
   for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4 *>(&KV[lt][32 * i + 8 * lp]) = vraw[i];
-  __syncthreads();
+  lds_sync();
   // ---- U ------------------------------------------------------------------
   {
     frag au[KS_C];

@@ -319,39 +319,57 @@ __global__ void __launch_bounds__(64) state_kernel(Args a) {
 }
 
 
-// One chunk's operands for a tile group, in flight in one loader wave's
-// registers: 16-byte pieces of the W and Ktilde blocks and of the group's U
-// tiles, in the order they sit in the LDS slot.
-template <typename T, int D, int NCW>
-struct ChunkLoader {
+// Loader waves per workgroup of the bf16 state pass.
+#ifndef GDN_STATE_NLW
+#define GDN_STATE_NLW 6
+#endif
+// loader waves that store one chunk into LDS together
+#ifndef GDN_STATE_TEAM
+#define GDN_STATE_TEAM 3
+#endif
+
+// One chunk's operands split over the TEAM loader waves of a team: wave part p
+// of the team holds the 16-byte pieces i = p (mod TEAM) of the chunk's LDS
+// slot, so storing a chunk into LDS takes TEAM waves in parallel.
+template <typename T, int D, int NCW, int TEAM>
+struct TeamLoader {
   using SG = SlotGeo<T, D, NCW>;
   static constexpr int64_t BLK = Geo<T, D>::W_ELEMS * sizeof(T) / 16;  // u32x4 per block
-  u32x4 v[SG::NV];
+  static constexpr int PPW = (SG::NV + TEAM - 1) / TEAM;              // pieces per wave
+  u32x4 v[PPW];
   float glog;
   int64_t uoff;
-  int lane;
+  int lane, part;
 
-  __device__ __forceinline__ void init(const Args &a, int jg, int ln) {
+  __device__ __forceinline__ void init(int jg, int ln, int pt) {
     uoff = (int64_t)jg * NCW * (SG::U_TILE_BYTES / 16);
     lane = ln;
+    part = pt;
   }
   __device__ __forceinline__ void issue(const Args &a, int64_t ch) {
     const u32x4 *__restrict__ wf = reinterpret_cast<const u32x4 *>(a.Wf) + ch * BLK + lane;
     const u32x4 *__restrict__ kf = reinterpret_cast<const u32x4 *>(a.Kf) + ch * BLK + lane;
     const u32x4 *__restrict__ uf = reinterpret_cast<const u32x4 *>(a.Uf) + ch * BLK + uoff + lane;
 #pragma unroll
-    for (int i = 0; i < SG::NV_W; ++i) v[i] = wf[i * 64];
-#pragma unroll
-    for (int i = 0; i < SG::NV_W; ++i) v[SG::NV_W + i] = kf[i * 64];
-#pragma unroll
-    for (int i = 0; i < SG::NV_U; ++i) v[2 * SG::NV_W + i] = uf[i * 64];
-    glog = a.Gw[ch * kChunk + (kChunk - 1)];
+    for (int m = 0; m < PPW; ++m) {
+      const int i = part + TEAM * m;
+      if (SG::NV % TEAM == 0 || i < SG::NV) {
+        const u32x4 *src = i < SG::NV_W ? wf + (int64_t)i * 64
+                         : i < 2 * SG::NV_W ? kf + (int64_t)(i - SG::NV_W) * 64
+                                            : uf + (int64_t)(i - 2 * SG::NV_W) * 64;
+        v[m] = *src;
+      }
+    }
+    if (part == 0) glog = a.Gw[ch * kChunk + (kChunk - 1)];
   }
-  __device__ __forceinline__ void drop(unsigned char *slot, int ln) const {
-    u32x4 *dst = reinterpret_cast<u32x4 *>(slot) + ln;
+  __device__ __forceinline__ void drop(unsigned char *slot) const {
+    u32x4 *dst = reinterpret_cast<u32x4 *>(slot) + lane;
 #pragma unroll
-    for (int i = 0; i < SG::NV; ++i) dst[i * 64] = v[i];
-    if (ln == 0) *reinterpret_cast<float *>(slot + SG::G_OFF) = glog;
+    for (int m = 0; m < PPW; ++m) {
+      const int i = part + TEAM * m;
+      if (SG::NV % TEAM == 0 || i < SG::NV) dst[i * 64] = v[m];
+    }
+    if (part == 0 && lane == 0) *reinterpret_cast<float *>(slot + SG::G_OFF) = glog;
   }
 };
 
@@ -360,9 +378,10 @@ struct ChunkLoader {
 // loader waves keep the operands of upcoming chunks in flight in their own
 // registers.  Loader w owns chunks c = w (mod NLW): it issues chunk c's loads
 // NLW steps ahead and drops the data into LDS slot c % 2 during step c, while
-// the compute waves work on chunk c - 1 from the other slot.  One barrier per
-// step orders the two.  The compute waves share every W / Ktilde fragment
-// they read.
+// the compute waves work on chunk c - 1 from the other slot.  One LDS-only
+// barrier per step orders the two (a full barrier would also wait for the
+// loads in flight and undo the look-ahead).  The compute waves share every
+// W / Ktilde fragment they read.
 template <typename T, int D, int NCW, int NLW>
 __global__ void __launch_bounds__(64 * (NCW + NLW)) state_kernel_pipe(Args a) {
   constexpr int NT = D / 16;
@@ -398,7 +417,7 @@ __global__ void __launch_bounds__(64 * (NCW + NLW)) state_kernel_pipe(Args a) {
     read_state<D>(a, row_ok, row, h, vcol, g, S);
     const int64_t ck_base = a.ck_every > 0 ? ld_index(a.ck_cs, a.ck_cs_type, seq) : 0;
     for (int st = 0; st <= nc; ++st) {
-      __syncthreads();
+      lds_sync();
       if (st == 0) continue;
       const int cc = st - 1;
       const LdsOps<T, D, NCW> op{slots[cc & 1], lane, wave};
@@ -415,16 +434,22 @@ __global__ void __launch_bounds__(64 * (NCW + NLW)) state_kernel_pipe(Args a) {
     if (a.out_final && a.outst && row_ok)
       write_state<T, D>(a.outst, a.out_dtype, a.out_str, row, h, vcol, g, S);
   } else {
-    // ---------------- loader wave ------------------------------------------
-    const int lw = wave - NCW;
-    ChunkLoader<T, D, NCW> ld;
-    ld.init(a, jg, lane);
-    if (lw < nc) ld.issue(a, ch0 + (int64_t)lw);
+    // ---------------- loader waves -----------------------------------------
+    // NLW / TEAM teams; team j owns chunks c = j (mod NLW / TEAM) and its
+    // TEAM waves load and store each of them together.  The loads stay in
+    // flight across the LDS-only barriers, so they have NLW / TEAM steps to
+    // arrive.
+    constexpr int NTEAM = NLW / GDN_STATE_TEAM;
+    static_assert(NLW % GDN_STATE_TEAM == 0, "loader waves split into whole teams");
+    const int lw = wave - NCW, team = lw / GDN_STATE_TEAM;
+    TeamLoader<T, D, NCW, GDN_STATE_TEAM> ld;
+    ld.init(jg, lane, lw % GDN_STATE_TEAM);
+    if (team < nc) ld.issue(a, ch0 + (int64_t)team);
     for (int st = 0; st <= nc; ++st) {
-      __syncthreads();
-      if (st < nc && st % NLW == lw) {
-        ld.drop(slots[st & 1], lane);
-        if (st + NLW < nc) ld.issue(a, ch0 + (int64_t)(st + NLW));
+      lds_sync();
+      if (st < nc && st % NTEAM == team) {
+        ld.drop(slots[st & 1]);
+        if (st + NTEAM < nc) ld.issue(a, ch0 + (int64_t)(st + NTEAM));
       }
     }
   }
@@ -440,14 +465,6 @@ static hipError_t launch_state_t(const Args &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Workgroup shape of the bf16 state pass: compute waves (16-column tiles)
-// and loader waves per workgroup.
-#ifndef GDN_STATE_NCW
-#define GDN_STATE_NCW 2
-#endif
-#ifndef GDN_STATE_NLW
-#define GDN_STATE_NLW 6
-#endif
 
 template <typename T, int D, int NCW, int NLW>
 static hipError_t launch_state_pipe_t(const Args &a, hipStream_t s) {
@@ -461,10 +478,18 @@ static hipError_t launch_state_pipe_t(const Args &a, hipStream_t s) {
 
 hipError_t launch_state(const Args &a, hipStream_t s) {
   if (a.dtype == GDN_BF16) {
-    constexpr int NCW = GDN_STATE_NCW, NLW = GDN_STATE_NLW;
-    if (a.D == 128) return launch_state_pipe_t<bf16, 128, NCW, NLW>(a, s);
-    if (a.D == 64) return launch_state_pipe_t<bf16, 64, (NCW < 4 ? NCW : 4), NLW>(a, s);
-    return launch_state_pipe_t<bf16, 32, (NCW < 2 ? NCW : 2), NLW>(a, s);
+    constexpr int NLW = GDN_STATE_NLW;
+    // One compute wave (16 columns) per workgroup while the workgroups fit on
+    // the CUs at once: that halves each CU's LDS traffic per column.  With
+    // more (sequence, head) pairs than that, two compute waves per workgroup
+    // halve the number of workgroups instead.
+    const int64_t units = (int64_t)a.N * a.H;
+    const bool wide = units * (a.D / 16) > (int64_t)a.num_cus;
+    if (a.D == 128)
+      return wide ? launch_state_pipe_t<bf16, 128, 2, NLW>(a, s) : launch_state_pipe_t<bf16, 128, 1, NLW>(a, s);
+    if (a.D == 64)
+      return wide ? launch_state_pipe_t<bf16, 64, 2, NLW>(a, s) : launch_state_pipe_t<bf16, 64, 1, NLW>(a, s);
+    return wide ? launch_state_pipe_t<bf16, 32, 2, NLW>(a, s) : launch_state_pipe_t<bf16, 32, 1, NLW>(a, s);
   }
   if (a.D == 128) return launch_state_t<float, 128>(a, s);
   if (a.D == 64) return launch_state_t<float, 64>(a, s);
