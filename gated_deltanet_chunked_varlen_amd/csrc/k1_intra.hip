@@ -303,7 +303,7 @@ struct IntraSmemB {
 };
 
 template <int D>
-__global__ void __launch_bounds__(256) intra_kernel_bf16(Args a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) intra_kernel_bf16(Args a) {
   using M = Mfma<bf16>;
   typedef bf16x8 frag;
   constexpr int NT = D / 16, KS_D = D / 32, KS_C = 2, NV = D / 32;
