@@ -214,6 +214,69 @@ __device__ __forceinline__ void load_norm_row_bf16(const bf16 *row, int p, bool 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Sequence geometry of a small batch straight from cu_seqlens, held by one
+// wave: lane i <= N reads cu_seqlens[i].  The sanitisation is the chunk-index
+// builder's: starts are the running maximum of cu_seqlens clamped to [0, T];
+// sequence i has length start[i + 1] - start[i] and ceil(length / 64) chunks,
+// numbered sequence-major.  Every lane of the wave must call it.
+// ---------------------------------------------------------------------------
+struct SeqLane {
+  int64_t raw;   // cu_seqlens[lane] as given (lanes <= N)
+  int bos;       // sanitised start of sequence `lane` (lanes <= N)
+  int len;       // its length (lanes < N, else 0)
+  int cc0, cc1;  // chunks before it / up to and including it
+};
+
+__device__ __forceinline__ int64_t load_index_any(const void *p, int type, int64_t i) {
+  return type == 1 ? ((const int64_t *)p)[i] : (int64_t)((const int32_t *)p)[i];
+}
+
+__device__ __forceinline__ SeqLane seq_lane(const void *cu, int cu_type, int N, int64_t T,
+                                            int lane) {
+  SeqLane s;
+  int64_t x = 0;
+  s.raw = 0;
+  if (lane <= N) {
+    s.raw = cu ? load_index_any(cu, cu_type, lane) : (lane == 0 ? 0 : T);
+    x = s.raw < 0 ? 0 : (s.raw > T ? T : s.raw);
+  }
+  int bos = (int)x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(bos, o);
+    if (lane >= o) bos = bos > y ? bos : y;
+  }
+  const int nxt = __shfl_down(bos, 1);
+  s.bos = bos;
+  s.len = lane < N ? nxt - bos : 0;
+  const int nch = (s.len + kChunk - 1) / kChunk;
+  int cc = nch;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(cc, o);
+    if (lane >= o) cc += y;
+  }
+  s.cc1 = cc;
+  s.cc0 = cc - nch;
+  return s;
+}
+
+// (first token, length) of flat chunk f from a SeqLane wave; length 0 when f
+// is past the last chunk.  Wave-uniform results.
+__device__ __forceinline__ void chunk_from_lanes(const SeqLane &s, int N, int f, int lane,
+                                                 int &tok, int &len) {
+  const unsigned long long m = __ballot(lane < N && s.cc0 <= f && f < s.cc1);
+  tok = 0;
+  len = 0;
+  if (m) {
+    const int seq = __ffsll((long long)m) - 1;
+    const int b0 = __shfl(s.bos, seq), c0 = __shfl(s.cc0, seq), l0 = __shfl(s.len, seq);
+    tok = b0 + kChunk * (f - c0);
+    len = min(kChunk, b0 + l0 - tok);
+  }
+}
+
 // fp32 exp of a (non-positive) log-gate difference.
 __device__ __forceinline__ float gexp(float x) { return __expf(x); }
 

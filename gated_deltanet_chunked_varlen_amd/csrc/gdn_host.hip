@@ -287,6 +287,11 @@ static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *
   a.ck_cs_type = p->checkpoint_cu_starts_type;
   a.status = p->status;
   a.num_cus = num_cus;
+  a.cu = p->cu_seqlens;
+  a.cu_type = p->cu_seqlens_type;
+  // small batches: the kernels read the sequence geometry from cu_seqlens
+  // themselves and the chunk-index builder is not launched
+  a.direct = (a.N <= kDirectSeqs && a.cap > 0) ? 1 : 0;
   if (a.ck_every > 0 && !a.ck) a.ck_every = 0;
 
   auto mark = [&](int i) -> hipError_t {
@@ -294,7 +299,7 @@ static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *
     return hipSuccess;
   };
   hipError_t e = mark(0);
-  if (e == hipSuccess)
+  if (e == hipSuccess && !a.direct)
     e = launch_chunk_index(p->cu_seqlens, p->cu_seqlens_type, a.N, a.T, a.cap, a.chunk_idx,
                            a.cu_chunks, a.seq_bos, a.n_chunks, a.status,
                            a.ck_every > 0 ? a.ck_cs : nullptr, a.ck_cs_type, a.ck_every,

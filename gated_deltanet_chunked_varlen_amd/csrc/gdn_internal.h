@@ -4,7 +4,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/gdn_prefill.h"
+#include "gdn_common.h"
+
 namespace gdn {
+
+// Largest batch whose sequence geometry one wave64 holds (lane i = sequence i,
+// lane N = the end offset).
+constexpr int kDirectSeqs = 63;
 
 // Everything a kernel may read, passed by value.  Pointers are device
 // pointers; strides are in elements.
@@ -17,6 +24,12 @@ struct Args {
   float scale;
   int32_t l2norm;
   void *out;
+  // cu_seqlens (NULL: one sequence [0, T]); with direct != 0 the kernels
+  // derive sequence and chunk geometry from it themselves (N <= kDirectSeqs)
+  // and the tables below are not built
+  const void *cu;
+  int32_t cu_type;
+  int32_t direct;
   // chunk table (written by the chunk-index builder)
   int32_t *chunk_idx;  // [cap][2]
   int32_t *cu_chunks;  // [N+1]
@@ -51,6 +64,69 @@ struct Args {
   int32_t *status;
   int32_t num_cus;    // compute units of the device (launch shapes)
 };
+
+#ifdef __HIPCC__
+// Data checks of a small batch (direct mode), by one wave: the chunk-index
+// builder's checks on cu_seqlens, checkpoint_cu_starts and state_indices,
+// written to *status as one word.
+__device__ __forceinline__ void validate_direct(const Args &a, const SeqLane &s, int lane) {
+  const int N = a.N;
+  unsigned bits = 0;
+  const long long prev = __shfl_up((long long)s.raw, 1);
+  if (a.cu && lane <= N) {
+    if (s.raw < 0 || s.raw > a.T || (lane > 0 && s.raw < prev)) bits |= GDN_STATUS_CU_SEQLENS;
+  }
+  if (a.ck_cs && a.ck_every > 0) {
+    const int nck = lane < N ? s.len / a.ck_every : 0;
+    int inc = nck;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    if (lane <= N && load_index_any(a.ck_cs, a.ck_cs_type, lane) != (int64_t)(inc - nck))
+      bits |= GDN_STATUS_CHECKPOINT_STARTS;
+  }
+  if (a.sidx && lane < N) {
+    const int64_t r = load_index_any(a.sidx, a.sidx_type, lane);
+    if (r < 0 || r >= a.pool_rows) bits |= GDN_STATUS_STATE_INDEX;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) bits |= __shfl_xor(bits, o);
+  if (lane == 0) a.status[0] = (int32_t)bits;
+}
+
+// (first token, length) of flat chunk f for the calling wave: from the chunk
+// table, or in direct mode from cu_seqlens (length 0: no such chunk).  With
+// validate, the wave also runs the data checks of direct mode.
+__device__ __forceinline__ void chunk_geometry(const Args &a, int f, int lane, bool validate,
+                                               int &tok, int &len) {
+  if (a.direct) {
+    const SeqLane s = seq_lane(a.cu, a.cu_type, a.N, a.T, lane);
+    if (validate && a.status) validate_direct(a, s, lane);
+    chunk_from_lanes(s, a.N, f, lane, tok, len);
+  } else {
+    tok = a.chunk_tok[2 * f];
+    len = a.chunk_tok[2 * f + 1];
+  }
+}
+
+// First flat chunk, chunk count and length of sequence seq, for the calling
+// wave.
+__device__ __forceinline__ void seq_geometry(const Args &a, int seq, int lane, int &f0, int &nc,
+                                             int &len) {
+  if (a.direct) {
+    const SeqLane s = seq_lane(a.cu, a.cu_type, a.N, a.T, lane);
+    f0 = __shfl(s.cc0, seq);
+    nc = __shfl(s.cc1, seq) - f0;
+    len = __shfl(s.len, seq);
+  } else {
+    f0 = a.cu_chunks[seq];
+    nc = min(a.cu_chunks[seq + 1], a.n_chunks[0]) - f0;
+    len = a.seq_bos[seq + 1] - a.seq_bos[seq];
+  }
+}
+#endif
 
 // Chunk-index builder: one workgroup.
 hipError_t launch_chunk_index(const void *cu, int cu_type, int32_t N, int64_t T,

@@ -53,12 +53,12 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
   const int H = a.H;
   const int f = (int)(blockIdx.x / H), h = (int)(blockIdx.x % H);
   const int64_t ch = ws_index(f, h, a.cap);
-  if (f >= a.n_chunks[0]) return;
-  const int seq = a.chunk_idx[2 * f], cidx = a.chunk_idx[2 * f + 1];
-  const int64_t bos = (int64_t)a.seq_bos[seq] + (int64_t)kChunk * cidx;
-  const int len = (int)min<int64_t>(kChunk, (int64_t)a.seq_bos[seq + 1] - bos);
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tb, len;
+  chunk_geometry(a, f, lane, blockIdx.x == 0 && wave == 0, tb, len);
+  if (len <= 0) return;
+  const int64_t bos = tb;
+
   const int g = lane >> 4, c = lane & 15;
   float(*AT)[68] = sm.AT;
 
@@ -313,12 +313,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
 
   const int H = a.H;
   const int f = (int)(blockIdx.x / H), h = (int)(blockIdx.x % H);
-  const int tb = a.chunk_tok[2 * f], len = a.chunk_tok[2 * f + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tb, len;
+  chunk_geometry(a, f, lane, blockIdx.x == 0 && wave == 0, tb, len);
   if (len <= 0) return;
   const int64_t bos = tb;
   const int64_t ch = ws_index(f, h, a.cap);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   float(*AT)[68] = sm.AT;
   bf16(*KV)[LDK] = sm.KV;

@@ -262,9 +262,8 @@ __global__ void __launch_bounds__(64) state_kernel(Args a) {
   const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
   const int vcol = 16 * jv + c;
 
-  const int f0 = a.cu_chunks[seq];
-  const int nc = min(a.cu_chunks[seq + 1], a.n_chunks[0]) - f0;
-  const int len = a.seq_bos[seq + 1] - a.seq_bos[seq];
+  int f0, nc, len;
+  seq_geometry(a, seq, lane, f0, nc, len);
 
   int64_t row = seq;
   bool row_ok = true;
@@ -398,9 +397,8 @@ __global__ void __launch_bounds__(64 * (NCW + NLW)) state_kernel_pipe(Args a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
 
-  const int f0 = a.cu_chunks[seq];
-  const int nc = min(a.cu_chunks[seq + 1], a.n_chunks[0]) - f0;
-  const int len = a.seq_bos[seq + 1] - a.seq_bos[seq];
+  int f0, nc, len;
+  seq_geometry(a, seq, lane, f0, nc, len);
   const int64_t ch0 = ws_index(f0, h, a.cap);
 
   if (wave < NCW) {

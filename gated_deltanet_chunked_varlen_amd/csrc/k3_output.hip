@@ -49,10 +49,11 @@ __global__ void __launch_bounds__(256) output_kernel(Args a) {
   const int H = a.H;
   const int f = (int)(blockIdx.x / H), h = (int)(blockIdx.x % H);
   const int64_t ch = ws_index(f, h, a.cap);
-  const int len = a.chunk_tok[2 * f + 1];
-  if (len <= 0) return;
-  const int64_t bos = a.chunk_tok[2 * f];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tb, len;
+  chunk_geometry(a, f, lane, false, tb, len);
+  if (len <= 0) return;
+  const int64_t bos = tb;
   const int g = lane >> 4, c = lane & 15;
 
   // this wave's value tiles: chunk-start state and new-value fragments,
@@ -222,10 +223,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) o
   const int H = a.H;
   const int f = (int)(blockIdx.x / H), h = (int)(blockIdx.x % H);
   const int64_t ch = ws_index(f, h, a.cap);
-  const int len = a.chunk_tok[2 * f + 1];
-  if (len <= 0) return;
-  const int64_t bos = a.chunk_tok[2 * f];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tb, len;
+  chunk_geometry(a, f, lane, false, tb, len);
+  if (len <= 0) return;
+  const int64_t bos = tb;
   const int g = lane >> 4, c = lane & 15;
 
   // this wave's value tiles: chunk-start state and new-value fragments,

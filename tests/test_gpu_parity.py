@@ -240,6 +240,33 @@ def test_status_checkpoint_starts_mismatch():
     assert gpu["status"] & 2
 
 
+def test_many_sequences_chunk_table_path():
+    # more sequences than one wave holds: the chunk-index builder's tables
+    # drive every kernel (fewer use the geometry straight from cu_seqlens)
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.integers(0, 150, size=100)]
+    lengths[5] = lengths[40] = 0
+    wl = _small(31, lengths, D=64, init="pool", pool_size=128, checkpoint_every=64)
+    gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] == 0
+    _check(wl, gpu, tl.run_oracle(wl))
+
+
+@pytest.mark.parametrize("nseq", [3, 80])
+def test_status_bad_cu_seqlens_full_call(nseq):
+    # a decreasing offset is flagged on both geometry paths (up to 63
+    # sequences the kernels check it themselves, beyond that the builder
+    # does), and the call still completes
+    lengths = [40] * nseq
+    wl = _small(32, lengths)
+    cu = wl.cu_seqlens.copy()
+    cu[2] = cu[1] - 5
+    wl.cu_seqlens = cu
+    gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] & 1
+    assert np.isfinite(gpu["out"]).all()
+
+
 def test_host_errors_raise_before_launch():
     from gated_deltanet_chunked_varlen_amd import chunk_gated_delta_rule
     wl = _small(23, [64, 64])
