@@ -30,7 +30,8 @@ STATUS_CHUNK_CAPACITY = 8
 EXPORTS = [
     "gdn_abi_version", "gdn_status_string", "gdn_max_chunks",
     "gdn_prefill_workspace_size", "gdn_validate_host", "gdn_prefill",
-    "gdn_prefill_timed", "gdn_build_chunk_indices",
+    "gdn_prefill_timed", "gdn_build_chunk_indices", "gdn_decode",
+    "gdn_validate_decode_host",
 ]
 
 _i64x4 = ctypes.c_int64 * 4
@@ -106,6 +107,10 @@ def lib():
         L.gdn_prefill_timed.restype = ctypes.c_int
         L.gdn_prefill_timed.argtypes = [ctypes.POINTER(Params), ctypes.c_void_p,
                                         ctypes.c_void_p * 5]
+        L.gdn_decode.restype = ctypes.c_int
+        L.gdn_decode.argtypes = [ctypes.POINTER(Params), ctypes.c_void_p]
+        L.gdn_validate_decode_host.restype = ctypes.c_int
+        L.gdn_validate_decode_host.argtypes = [ctypes.POINTER(Params)]
         L.gdn_build_chunk_indices.restype = ctypes.c_int
         L.gdn_build_chunk_indices.argtypes = [
             ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,

@@ -70,9 +70,10 @@ def make_params(q, k, v, g=None, beta=None, scale=None, initial_state=None,
                 use_qk_l2norm_in_kernel=False, output=None, output_state=None,
                 state_checkpoints=None, checkpoint_cu_starts=None,
                 checkpoint_every_n_tokens=0, state_indices=None,
-                max_seqlen=None, status=None):
+                max_seqlen=None, status=None, decode=False):
     """Fill the C parameter block (allocates output / final state when the
-    caller passes none).  Returns (params, output, output_state, keep)."""
+    caller passes none).  Returns (params, output, output_state).  With
+    ``decode`` token i is sequence i's one new token (num_seqs = T)."""
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors")
     dev = q.device
@@ -107,7 +108,11 @@ def make_params(q, k, v, g=None, beta=None, scale=None, initial_state=None,
     p.g, p.beta = _ptr(g), _ptr(beta)
     p.has_scale = 0 if scale is None else 1
     p.scale = 0.0 if scale is None else float(scale)
-    if cu_seqlens is not None:
+    if decode:
+        if cu_seqlens is not None:
+            raise ValueError("decode takes one token per sequence and no cu_seqlens")
+        N = T
+    elif cu_seqlens is not None:
         p.cu_seqlens_type = _index("cu_seqlens", cu_seqlens)
         p.cu_seqlens = _ptr(cu_seqlens)
         N = cu_seqlens.numel() - 1
@@ -210,6 +215,30 @@ def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None,
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = lib.gdn_prefill(ctypes.byref(p), ctypes.c_void_p(stream))
+    if rc != 0:
+        _raise(rc)
+    if output_final_state:
+        return output, output_state
+    return output
+
+
+def gated_delta_rule_decode(q, k, v, g=None, beta=None, scale=None,
+                            initial_state=None, output_final_state=True,
+                            use_qk_l2norm_in_kernel=False, output=None,
+                            output_state=None, state_indices=None, status=None):
+    """One decode step: token i of q/k/v [N, heads, D] is the new token of
+    sequence i; g, beta [N, H].  The state pool semantics are those of
+    ``chunk_gated_delta_rule`` (with ``state_indices`` the final state is the
+    pool ``output_state``; it may be ``initial_state`` itself).  Returns
+    ``output`` [N, H, D], or ``(output, final_state)``."""
+    lib = nat.lib()
+    p, output, output_state = make_params(
+        q, k, v, g, beta, scale, initial_state, output_final_state, None,
+        use_qk_l2norm_in_kernel, output, output_state, None, None, 0,
+        state_indices, None, status, decode=True)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.gdn_decode(ctypes.byref(p), ctypes.c_void_p(stream))
     if rc != 0:
         _raise(rc)
     if output_final_state:

@@ -224,18 +224,11 @@ int gdn_build_chunk_indices(const void *cu_seqlens, int32_t cu_type, int32_t num
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
-static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *events) {
-  int rc = gdn_validate_host(p);
-  if (rc != GDN_OK) return rc;
-  int num_cus = 0;
-  rc = check_device(&num_cus);
-  if (rc != GDN_OK) return rc;
-  hipStream_t s = (hipStream_t)stream;
-  const Layout L = plan(p);
+// The kernels' argument block for a call (workspace pointers only when a
+// workspace layout is given).
+static void fill_args(const gdn_prefill_params *p, const Layout *L, int num_cus, Args &a) {
   unsigned char *ws = (unsigned char *)p->workspace;
   const int64_t H = sab_heads(p), D = p->head_size;
-
-  Args a;
   std::memset(&a, 0, sizeof(a));
   a.T = p->total_tokens;
   a.N = p->num_seqs;
@@ -253,18 +246,20 @@ static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *
   a.scale = p->has_scale ? p->scale : (float)(1.0 / std::sqrt((double)D));
   a.l2norm = p->use_qk_l2norm_in_kernel ? 1 : 0;
   a.out = p->output;
-  a.chunk_idx = (int32_t *)(ws + L.chunk_idx);
-  a.chunk_tok = (int32_t *)(ws + L.chunk_tok);
-  a.cu_chunks = (int32_t *)(ws + L.cu_chunks);
-  a.seq_bos = (int32_t *)(ws + L.seq_bos);
-  a.n_chunks = (int32_t *)(ws + L.n_chunks);
+  if (L) {
+    a.chunk_idx = (int32_t *)(ws + L->chunk_idx);
+    a.chunk_tok = (int32_t *)(ws + L->chunk_tok);
+    a.cu_chunks = (int32_t *)(ws + L->cu_chunks);
+    a.seq_bos = (int32_t *)(ws + L->seq_bos);
+    a.n_chunks = (int32_t *)(ws + L->n_chunks);
+    a.Wf = ws + L->Wf;
+    a.Kf = ws + L->Kf;
+    a.Uf = ws + L->Uf;
+    a.Hf = ws + L->Hf;
+    a.Nf = ws + L->Nf;
+    a.Gw = (float *)(ws + L->Gw);
+  }
   a.cap = gdn_max_chunks(p->total_tokens, p->num_seqs);
-  a.Wf = ws + L.Wf;
-  a.Kf = ws + L.Kf;
-  a.Uf = ws + L.Uf;
-  a.Hf = ws + L.Hf;
-  a.Nf = ws + L.Nf;
-  a.Gw = (float *)(ws + L.Gw);
   const int64_t rows = p->state_indices ? p->pool_size : p->num_seqs;
   a.init = p->initial_state;
   a.init_dtype = p->initial_state_dtype;
@@ -293,6 +288,18 @@ static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *
   // themselves and the chunk-index builder is not launched
   a.direct = (a.N <= kDirectSeqs && a.cap > 0) ? 1 : 0;
   if (a.ck_every > 0 && !a.ck) a.ck_every = 0;
+}
+
+static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *events) {
+  int rc = gdn_validate_host(p);
+  if (rc != GDN_OK) return rc;
+  int num_cus = 0;
+  rc = check_device(&num_cus);
+  if (rc != GDN_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const Layout L = plan(p);
+  Args a;
+  fill_args(p, &L, num_cus, a);
 
   auto mark = [&](int i) -> hipError_t {
     if (events && events[i]) return hipEventRecord((hipEvent_t)events[i], s);
@@ -316,6 +323,48 @@ static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *
 
 int gdn_prefill(const gdn_prefill_params *p, void *stream) {
   return prefill_impl(p, stream, nullptr);
+}
+
+int gdn_validate_decode_host(const gdn_prefill_params *p) {
+  if (!p) return GDN_ERR_NULL;
+  if (p->num_seqs < 0 || p->total_tokens != p->num_seqs || p->cu_seqlens) return GDN_ERR_SHAPE;
+  if (p->num_q_heads < 1 || p->num_k_heads < 1 || p->num_v_heads < 1) return GDN_ERR_SHAPE;
+  if (p->head_size != 32 && p->head_size != 64 && p->head_size != 128) return GDN_ERR_SHAPE;
+  const int32_t hq = p->num_q_heads, hk = p->num_k_heads, hv = p->num_v_heads;
+  if (!((hq == hk && hv % hq == 0) || (hk == hv && hq % hk == 0))) return GDN_ERR_HEAD_RATIO;
+  if (p->qkv_dtype != GDN_F32 && p->qkv_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+  if (p->checkpoint_every_n_tokens != 0 || p->state_checkpoints || p->checkpoint_cu_starts)
+    return GDN_ERR_CHECKPOINT;
+  const int64_t N = p->num_seqs, H = sab_heads(p), D = p->head_size;
+  if (N > 0 && (!p->q || !p->k || !p->v || !p->output)) return GDN_ERR_NULL;
+  if (p->initial_state && !valid_state_dtype(p->initial_state_dtype)) return GDN_ERR_DTYPE;
+  if (p->output_final_state) {
+    if (!p->output_state) return GDN_ERR_STATE;
+    if (!valid_state_dtype(p->output_state_dtype)) return GDN_ERR_DTYPE;
+  }
+  int64_t rows = N;
+  if (p->state_indices) {
+    if (!valid_itype(p->state_indices_type)) return GDN_ERR_DTYPE;
+    if (p->pool_size < 1) return GDN_ERR_STATE;
+    rows = p->pool_size;
+  }
+  if (p->initial_state && !strides_ok(p->initial_state_strides, rows, H, D)) return GDN_ERR_STRIDES;
+  if (p->output_final_state && !strides_ok(p->output_state_strides, rows, H, D)) return GDN_ERR_STRIDES;
+  return GDN_OK;
+}
+
+int gdn_decode(const gdn_prefill_params *p, void *stream) {
+  int rc = gdn_validate_decode_host(p);
+  if (rc != GDN_OK) return rc;
+  int num_cus = 0;
+  rc = check_device(&num_cus);
+  if (rc != GDN_OK) return rc;
+  Args a;
+  fill_args(p, nullptr, num_cus, a);
+  a.direct = 0;
+  if (a.N == 0 && !a.status) return GDN_OK;
+  const hipError_t e = launch_decode(a, (hipStream_t)stream);
+  return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
 int gdn_prefill_timed(const gdn_prefill_params *p, void *stream, void *const events[5]) {

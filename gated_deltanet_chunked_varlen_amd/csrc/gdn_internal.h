@@ -138,5 +138,6 @@ hipError_t launch_chunk_index(const void *cu, int cu_type, int32_t N, int64_t T,
 hipError_t launch_intra(const Args &a, hipStream_t s);
 hipError_t launch_state(const Args &a, hipStream_t s);
 hipError_t launch_output(const Args &a, hipStream_t s);
+hipError_t launch_decode(const Args &a, hipStream_t s);
 
 }  // namespace gdn

@@ -162,6 +162,30 @@ int gdn_prefill_timed(const gdn_prefill_params *p, void *stream,
                       void *const events[5]);
 
 /*
+ * One decode step: one new token per sequence, applied to the state with the
+ * recurrence itself, no chunking (weigao.cc "GDN 与 Chunked Prefill", section
+ * "Prefill 和 decode 的差异": after prefill each step adds a single token,
+ * S <- alpha (I - beta k k^T) S + beta k v^T and o = scale * S^T q with the
+ * updated S; gitcode "FlashInfer GDN Prefill 完全指南", sections "GDN
+ * prefill" and "状态池": decode continues from the state prefill leaves, in
+ * the same [rows, H, V, K] layout and state_indices pool).
+ *
+ * Takes the prefill parameter block with these differences:
+ *   - token i is the new token of sequence i: total_tokens == num_seqs, and
+ *     cu_seqlens must be NULL (GDN_ERR_SHAPE otherwise); q/k/v are
+ *     [N, heads, D], g and beta [N, H], output [N, H, D];
+ *   - checkpoint_every_n_tokens must be 0 and the checkpoint buffers NULL
+ *     (GDN_ERR_CHECKPOINT); max_seqlen and the workspace are ignored.
+ * States, pools (output_state may alias initial_state), head sharing,
+ * defaults, l2 normalisation and the status word behave as in gdn_prefill;
+ * only GDN_STATUS_STATE_INDEX can be set.  Duplicate state_indices race.
+ */
+int gdn_decode(const gdn_prefill_params *p, void *stream);
+
+/* The host-side checks of gdn_decode() alone; no GPU needed. */
+int gdn_validate_decode_host(const gdn_prefill_params *p);
+
+/*
  * The device-side chunk-index builder alone (weigao.cc, sections "chunked
  * prefill 有两层含义" and "为什么 trace 里它可能看起来很贵": the flat chunk ->
  * (sequence, chunk) table built on the device, with no device-to-host copy).

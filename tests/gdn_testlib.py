@@ -126,6 +126,42 @@ def expected_pool(wl, orc_final):
     return pool
 
 
+def run_gpu_decode(wl, device="cuda", status=False):
+    """One decode step on the HIP path for a workload whose sequences all have
+    length 1 (token i = sequence i); same return dict as run_gpu."""
+    torch = _torch()
+    from gated_deltanet_chunked_varlen_amd import gated_delta_rule_decode
+    assert all(int(x) == 1 for x in np.diff(wl.cu_seqlens))
+    d = to_device(wl, device)
+    H, D, N = wl.H, wl.D, wl.N
+    sdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+    kw = dict(g=d["g"], beta=d["beta"], scale=wl.scale,
+              use_qk_l2norm_in_kernel=wl.l2norm_in_kernel,
+              output_final_state=wl.output_final_state)
+    pool_before = None
+    if wl.state_indices is not None:
+        pool = d["initial_state"]
+        pool_before = pool.clone()
+        kw.update(initial_state=pool, state_indices=d["state_indices"],
+                  output_state=pool if wl.in_place_pool else torch.zeros_like(pool))
+    else:
+        kw.update(initial_state=d["initial_state"])
+        if wl.output_final_state:
+            kw.update(output_state=torch.zeros((N, H, D, D), dtype=sdt[wl.final_state_dtype],
+                                               device=device))
+    st = torch.full((1,), -1, dtype=torch.int32, device=device) if status else None
+    if st is not None:
+        kw["status"] = st
+    res = gated_delta_rule_decode(d["q"], d["k"], d["v"], **kw)
+    out, fin = (res if wl.output_final_state else (res, None))
+    torch.cuda.synchronize()
+    f64 = lambda x: None if x is None else x.float().cpu().numpy().astype(np.float64)
+    r = dict(out=f64(out), final=f64(fin), ckpt=None, pool_before=f64(pool_before))
+    if st is not None:
+        r["status"] = int(st.item())
+    return r
+
+
 def compare(wl, gpu, orc, heads=None):
     """Relative L2 errors of outputs / final states / checkpoints."""
     tol = TOL[wl.dtype]

@@ -164,3 +164,27 @@ def test_workspace_size_zero_for_bad_shape():
     nat = _lib()
     p = _params(D=48)
     assert nat.lib().gdn_prefill_workspace_size(ctypes.byref(p)) == 0
+
+
+def _validate_decode(p):
+    return _lib().lib().gdn_validate_decode_host(ctypes.byref(p))
+
+
+def test_validate_decode_ok():
+    assert _validate_decode(_params(T=64, N=64, cu=False)) == 0
+    assert _validate_decode(_params(T=0, N=0, cu=False)) == 0
+    assert _validate_decode(_params(T=8, N=8, cu=False, hq=8, hk=4, hv=4)) == 0
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(T=64, N=32, cu=False), "GDN_ERR_SHAPE"),        # one token per sequence
+    (dict(T=8, N=8, cu=True), "GDN_ERR_SHAPE"),           # no cu_seqlens
+    (dict(T=8, N=8, cu=False, D=48), "GDN_ERR_SHAPE"),
+    (dict(T=8, N=8, cu=False, hq=4, hk=2, hv=4), "GDN_ERR_HEAD_RATIO"),
+    (dict(T=8, N=8, cu=False, dtype=2), "GDN_ERR_DTYPE"),
+    (dict(T=8, N=8, cu=False, extra=dict(checkpoint_every_n_tokens=64)), "GDN_ERR_CHECKPOINT"),
+    (dict(T=8, N=8, cu=False, extra=dict(output_final_state=1)), "GDN_ERR_STATE"),
+    (dict(T=8, N=8, cu=False, extra=dict(k=None)), "GDN_ERR_NULL"),
+])
+def test_validate_decode_errors(kw, err):
+    assert _validate_decode(_params(**kw)) == code(err)
