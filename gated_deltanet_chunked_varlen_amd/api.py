@@ -22,7 +22,8 @@ import torch
 
 from . import _native as nat
 
-_QKV_DTYPES = {torch.float32: nat.GDN_F32, torch.bfloat16: nat.GDN_BF16}
+_QKV_DTYPES = {torch.float32: nat.GDN_F32, torch.bfloat16: nat.GDN_BF16,
+               torch.float16: nat.GDN_F16}
 _STATE_DTYPES = {torch.float32: nat.GDN_F32, torch.bfloat16: nat.GDN_BF16,
                  torch.float16: nat.GDN_F16}
 _INDEX_TYPES = {torch.int32: nat.GDN_I32, torch.int64: nat.GDN_I64}
@@ -89,7 +90,7 @@ def make_params(q, k, v, g=None, beta=None, scale=None, initial_state=None,
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
     if q.dtype not in _QKV_DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+        raise ValueError("q, k, v must share dtype float32, bfloat16 or float16")
     T, hq, D = q.shape
     hk, hv = k.shape[1], v.shape[1]
     if k.shape[0] != T or v.shape[0] != T or k.shape[2] != D or v.shape[2] != D:

@@ -3,9 +3,10 @@
 //
 // Matrix products use the CDNA matrix cores:
 //   bf16: v_mfma_f32_16x16x32_bf16  (A 16x32, B 32x16, C 16x16 fp32)
+//   fp16: v_mfma_f32_16x16x32_f16   (same shapes)
 //   fp32: v_mfma_f32_16x16x4_f32    (A 16x4,  B 4x16,  C 16x16 fp32)
 // Lane l = 16*g + c (g = l / 16 in 0..3, c = l % 16).  With KPL contraction
-// elements per lane per instruction (8 for bf16, 1 for fp32):
+// elements per lane per instruction (8 for bf16 / fp16, 1 for fp32):
 //   A operand: lane holds A[c][KPL*g + e], e < KPL   (row c of the 16-row tile)
 //   B operand: lane holds B[KPL*g + e][c]            (column c)
 //   C result : lane holds C[4*g + r][c], r < 4
@@ -30,6 +31,9 @@ namespace gdn {
 typedef __bf16 bf16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef _Float16 f16;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 // 16-byte register vector; HIP's uint4 is a struct of unions that keeps
 // arrays of it out of registers, this native vector type does not.
@@ -54,6 +58,7 @@ template <typename T> struct Mfma;
 template <> struct Mfma<bf16> {
   static constexpr int KPL = 8;
   typedef bf16x8 frag;
+  typedef bf16x4 half;
   static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -63,6 +68,21 @@ template <> struct Mfma<bf16> {
   static __device__ __forceinline__ frag pack(const float *x) {
     const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
     return __builtin_convertvector(v, bf16x8);
+  }
+};
+
+template <> struct Mfma<f16> {
+  static constexpr int KPL = 8;
+  typedef f16x8 frag;
+  typedef f16x4 half;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void set(frag &f, int e, float x) { f[e] = (f16)x; }
+  static __device__ __forceinline__ float get(const frag &f, int e) { return (float)f[e]; }
+  static __device__ __forceinline__ frag pack(const float *x) {
+    const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+    return __builtin_convertvector(v, f16x8);
   }
 };
 
@@ -90,20 +110,24 @@ template <> struct Mfma<float> {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ i16x4 lds_read_tr4(const bf16 *p) {
+template <typename T>
+__device__ __forceinline__ i16x4 lds_read_tr4(const T *p) {
+  static_assert(sizeof(T) == 2, "16-bit elements");
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4 *)(p));
 }
 
 // Rows r0(g) .. r0(g) + 3 and r1(g) .. r1(g) + 3 of column col0 + c of a
-// row-major LDS matrix with leading dimension ld, as one bf16x8 fragment.
-__device__ __forceinline__ bf16x8 lds_col_frag(const bf16 *X, int ld, int r0, int r1,
-                                               int col0, int c) {
+// row-major 16-bit LDS matrix with leading dimension ld, as one operand
+// fragment.
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag lds_col_frag(const T *X, int ld, int r0,
+                                                               int r1, int col0, int c) {
   const int rr = c >> 2, cc = col0 + 4 * (c & 3);
   const i16x4 lo = lds_read_tr4(X + (r0 + rr) * ld + cc);
   const i16x4 hi = lds_read_tr4(X + (r1 + rr) * ld + cc);
   const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(typename Mfma<T>::frag, v);
 }
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
@@ -180,13 +204,15 @@ __device__ __forceinline__ void load_row_part(const Tin *row, int p, float (&x)[
   }
 }
 
-// bf16 row part of lane part p (the runs of load_row_part), optionally
-// normalised with row_inv_norm, rounded back to bf16: NV = D / 32 fragments
-// of 8 elements, fragment i holding row elements 32 i + 8 p .. + 7.  The
-// intra-chunk and output passes both use this, so they see the same k rows.
-template <int D>
-__device__ __forceinline__ void load_norm_row_bf16(const bf16 *row, int p, bool valid,
-                                                   bool l2norm, bf16x8 (&out)[D / 32]) {
+// 16-bit (bf16 / fp16) row part of lane part p (the runs of load_row_part),
+// optionally normalised with row_inv_norm, rounded back to the input type:
+// NV = D / 32 fragments of 8 elements, fragment i holding row elements
+// 32 i + 8 p .. + 7.  The intra-chunk and output passes both use this, so they
+// see the same k rows.
+template <typename T, int D>
+__device__ __forceinline__ void load_norm_row16(const T *row, int p, bool valid, bool l2norm,
+                                                typename Mfma<T>::frag (&out)[D / 32]) {
+  typedef typename Mfma<T>::frag frag;
   constexpr int NV = D / 32;
   u32x4 raw[NV];
 #pragma unroll
@@ -194,13 +220,13 @@ __device__ __forceinline__ void load_norm_row_bf16(const bf16 *row, int p, bool 
     raw[i] = valid ? *reinterpret_cast<const u32x4 *>(row + 32 * i + 8 * p) : u32x4{0, 0, 0, 0};
   if (!l2norm) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) out[i] = __builtin_bit_cast(bf16x8, raw[i]);
+    for (int i = 0; i < NV; ++i) out[i] = __builtin_bit_cast(frag, raw[i]);
     return;
   }
   float x[D / 4];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const bf16x8 r8 = __builtin_bit_cast(bf16x8, raw[i]);
+    const frag r8 = __builtin_bit_cast(frag, raw[i]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[8 * i + e] = (float)r8[e];
   }
@@ -210,7 +236,7 @@ __device__ __forceinline__ void load_norm_row_bf16(const bf16 *row, int p, bool 
     const f32x8 y = {x[8 * i] * inv,     x[8 * i + 1] * inv, x[8 * i + 2] * inv,
                      x[8 * i + 3] * inv, x[8 * i + 4] * inv, x[8 * i + 5] * inv,
                      x[8 * i + 6] * inv, x[8 * i + 7] * inv};
-    out[i] = __builtin_convertvector(y, bf16x8);
+    out[i] = __builtin_convertvector(y, frag);
   }
 }
 

@@ -156,7 +156,8 @@ static int check_shape(const gdn_prefill_params *p) {
   const bool gva = (hq == hk) && (hv % hq == 0);
   const bool gqa = (hk == hv) && (hq % hk == 0);
   if (!gva && !gqa) return GDN_ERR_HEAD_RATIO;
-  if (p->qkv_dtype != GDN_F32 && p->qkv_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+  if (p->qkv_dtype != GDN_F32 && p->qkv_dtype != GDN_BF16 && p->qkv_dtype != GDN_F16)
+    return GDN_ERR_DTYPE;
   return GDN_OK;
 }
 
@@ -332,7 +333,8 @@ int gdn_validate_decode_host(const gdn_prefill_params *p) {
   if (p->head_size != 32 && p->head_size != 64 && p->head_size != 128) return GDN_ERR_SHAPE;
   const int32_t hq = p->num_q_heads, hk = p->num_k_heads, hv = p->num_v_heads;
   if (!((hq == hk && hv % hq == 0) || (hk == hv && hq % hk == 0))) return GDN_ERR_HEAD_RATIO;
-  if (p->qkv_dtype != GDN_F32 && p->qkv_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+  if (p->qkv_dtype != GDN_F32 && p->qkv_dtype != GDN_BF16 && p->qkv_dtype != GDN_F16)
+    return GDN_ERR_DTYPE;
   if (p->checkpoint_every_n_tokens != 0 || p->state_checkpoints || p->checkpoint_cu_starts)
     return GDN_ERR_CHECKPOINT;
   const int64_t N = p->num_seqs, H = sab_heads(p), D = p->head_size;

@@ -287,7 +287,7 @@ static hipError_t launch_intra_t(const Args &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 variant.  k and v stay row-major in LDS and every product that
+// 16-bit (bf16 / fp16) variant.  k and v stay row-major in LDS and every product that
 // contracts over the chunk's rows reads them through transposed LDS reads
 // (lds_col_frag), so there is no transposed copy: one padded 64 x D bf16
 // buffer holds the normalised k rows and, once W and Ktilde^T are out, the v
@@ -295,21 +295,21 @@ static hipError_t launch_intra_t(const Args &a, hipStream_t s) {
 // workgroups share a CU.  The chunk's first token and length come from the
 // (first token, length) table in one load.
 // ---------------------------------------------------------------------------
-template <int D>
+template <typename T, int D>
 struct IntraSmemB {
   static constexpr int LDK = D + 16;  // row pitch in elements (32 B pad)
-  bf16 KV[64][LDK];                   // normalised k rows, later v rows
+  T KV[64][LDK];                   // normalised k rows, later v rows
   float AT[64][68];                   // A, then T; [t][64] = G, [t][65] = beta
 };
 
-template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) intra_kernel_bf16(Args a) {
-  using M = Mfma<bf16>;
-  typedef bf16x8 frag;
+template <typename T, int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) intra_kernel_h(Args a) {
+  using M = Mfma<T>;
+  typedef typename M::frag frag;
   constexpr int NT = D / 16, KS_D = D / 32, KS_C = 2, NV = D / 32;
-  constexpr int LDK = IntraSmemB<D>::LDK;
+  constexpr int LDK = IntraSmemB<T, D>::LDK;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  IntraSmemB<D> &sm = *reinterpret_cast<IntraSmemB<D> *>(smem_raw);
+  IntraSmemB<T, D> &sm = *reinterpret_cast<IntraSmemB<T, D> *>(smem_raw);
 
   const int H = a.H;
   const int f = (int)(blockIdx.x / H), h = (int)(blockIdx.x % H);
@@ -322,7 +322,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
 
   const int g = lane >> 4, c = lane & 15;
   float(*AT)[68] = sm.AT;
-  bf16(*KV)[LDK] = sm.KV;
+  T(*KV)[LDK] = sm.KV;
 
   // ---- k (normalised) into LDS, v kept in registers; gates ---------------
   const int lt = tid >> 2, lp = tid & 3;  // row and row part of this thread
@@ -330,12 +330,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
   {
     const bool valid = lt < len;
     const int kh = h / (H / a.hk), vh = h / (H / a.hv);
-    const bf16 *vrow = (const bf16 *)a.v + ((bos + lt) * a.hv + vh) * D;
+    const T *vrow = (const T *)a.v + ((bos + lt) * a.hv + vh) * D;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
       vraw[i] = valid ? *reinterpret_cast<const u32x4 *>(vrow + 32 * i + 8 * lp) : u32x4{0, 0, 0, 0};
     frag kn[NV];
-    load_norm_row_bf16<D>((const bf16 *)a.k + ((bos + lt) * a.hk + kh) * D, lp, valid,
+    load_norm_row16<T, D>((const T *)a.k + ((bos + lt) * a.hk + kh) * D, lp, valid,
                           a.l2norm != 0, kn);
 #pragma unroll
     for (int i = 0; i < NV; ++i) *reinterpret_cast<frag *>(&KV[lt][32 * i + 8 * lp]) = kn[i];
@@ -452,7 +452,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
       }
       bw[kt] = M::pack(y);
     }
-    bf16 *wf = (bf16 *)a.Wf + ch * (int64_t)(64 * D) + (int64_t)w * KS_D * 64 * 8;
+    T *wf = (T *)a.Wf + ch * (int64_t)(64 * D) + (int64_t)w * KS_D * 64 * 8;
     frag out[KS_D];
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt) {
@@ -467,7 +467,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = 4 * dt + r;
-        out[s / 8][s % 8] = (bf16)(-acc[r]);
+        out[s / 8][s % 8] = (T)(-acc[r]);
       }
     }
 #pragma unroll
@@ -477,7 +477,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
   // ---- Ktilde^T fragments: rows pi(g, 8kt + e) of k column 16 it2 + c ------
   {
     const float glast = AT[63][64];
-    bf16 *kf = (bf16 *)a.Kf + ch * (int64_t)(64 * D);
+    T *kf = (T *)a.Kf + ch * (int64_t)(64 * D);
 #pragma unroll
     for (int q = 0; q < NT * KS_C / 4; ++q) {
       const int fidx = wave + 4 * q;  // fragment block (row tile it2, k-step kt)
@@ -510,7 +510,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
       }
       au[kt] = M::pack(y);
     }
-    bf16 *uf = (bf16 *)a.Uf + ch * (int64_t)(64 * D);
+    T *uf = (T *)a.Uf + ch * (int64_t)(64 * D);
 #pragma unroll
     for (int jv = 0; jv < NT; ++jv) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -519,36 +519,41 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
         const frag fb = lds_col_frag(&KV[0][0], LDK, kt * 32 + g * 8, kt * 32 + g * 8 + 4, 16 * jv, c);
         acc = M::mma(au[kt], fb, acc);
       }
-      bf16 *dst = uf + (((int64_t)jv * 4 + w) * 64 + lane) * 4;
-      bf16x4 o4;
+      T *dst = uf + (((int64_t)jv * 4 + w) * 64 + lane) * 4;
+      typename M::half o4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o4[r] = (bf16)acc[r];
-      *reinterpret_cast<bf16x4 *>(dst) = o4;
+      for (int r = 0; r < 4; ++r) o4[r] = (T)acc[r];
+      *reinterpret_cast<typename M::half *>(dst) = o4;
     }
   }
 }
 
-template <int D>
-static hipError_t launch_intra_bf16(const Args &a, hipStream_t s) {
-  const size_t smem = sizeof(IntraSmemB<D>);
+template <typename T, int D>
+static hipError_t launch_intra_h(const Args &a, hipStream_t s) {
+  const size_t smem = sizeof(IntraSmemB<T, D>);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)intra_kernel_bf16<D>,
+    hipError_t e = hipFuncSetAttribute((const void *)intra_kernel_h<T, D>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t blocks = a.cap * a.H;
   if (blocks == 0) return hipSuccess;
-  intra_kernel_bf16<D><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
+  intra_kernel_h<T, D><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_intra(const Args &a, hipStream_t s) {
   if (a.dtype == GDN_BF16) {
-    if (a.D == 128) return launch_intra_bf16<128>(a, s);
-    if (a.D == 64) return launch_intra_bf16<64>(a, s);
-    return launch_intra_bf16<32>(a, s);
+    if (a.D == 128) return launch_intra_h<bf16, 128>(a, s);
+    if (a.D == 64) return launch_intra_h<bf16, 64>(a, s);
+    return launch_intra_h<bf16, 32>(a, s);
+  }
+  if (a.dtype == GDN_F16) {
+    if (a.D == 128) return launch_intra_h<f16, 128>(a, s);
+    if (a.D == 64) return launch_intra_h<f16, 64>(a, s);
+    return launch_intra_h<f16, 32>(a, s);
   }
   if (a.D == 128) return launch_intra_t<float, 128>(a, s);
   if (a.D == 64) return launch_intra_t<float, 64>(a, s);

@@ -475,6 +475,16 @@ static hipError_t launch_state_pipe_t(const Args &a, hipStream_t s) {
 }
 
 hipError_t launch_state(const Args &a, hipStream_t s) {
+  if (a.dtype == GDN_F16) {
+    constexpr int NLW = GDN_STATE_NLW;
+    const int64_t units = (int64_t)a.N * a.H;
+    const bool wide = units * (a.D / 16) > (int64_t)a.num_cus;
+    if (a.D == 128)
+      return wide ? launch_state_pipe_t<f16, 128, 2, NLW>(a, s) : launch_state_pipe_t<f16, 128, 1, NLW>(a, s);
+    if (a.D == 64)
+      return wide ? launch_state_pipe_t<f16, 64, 2, NLW>(a, s) : launch_state_pipe_t<f16, 64, 1, NLW>(a, s);
+    return wide ? launch_state_pipe_t<f16, 32, 2, NLW>(a, s) : launch_state_pipe_t<f16, 32, 1, NLW>(a, s);
+  }
   if (a.dtype == GDN_BF16) {
     constexpr int NLW = GDN_STATE_NLW;
     // One compute wave (16 columns) per workgroup while the workgroups fit on

@@ -192,7 +192,7 @@ static hipError_t launch_output_t(const Args &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 variant.  The same products, computed transposed: O^T = S^T (diag(exp
+// 16-bit (bf16 / fp16) variant.  The same products, computed transposed: O^T = S^T (diag(exp
 // G) Q)^T + N^T P^T.  The stored chunk-start state and new values are already
 // in the operand layout this needs, so every lane ends up holding four
 // consecutive output columns of one row and stores them as one 8-byte write;
@@ -200,25 +200,25 @@ static hipError_t launch_output_t(const Args &a, hipStream_t s) {
 // has finished reading k, so q, k/P and the gates take about 35 KB at
 // D = 128 and four workgroups share a CU.
 // ---------------------------------------------------------------------------
-template <int D>
+template <typename T, int D>
 struct OutSmemB {
   static constexpr int LDQ = D + 8;
-  bf16 Qs[64][LDQ];
+  T Qs[64][LDQ];
   union {
-    bf16 Ks[64][LDQ];         // k rows, for P
-    bf16x8 Pf[4][2][64];      // P rows as operand fragments, after P
+    T Ks[64][LDQ];         // k rows, for P
+    typename Mfma<T>::frag Pf[4][2][64];      // P rows as operand fragments, after P
   } kp;
   float Gs[64];
 };
 
-template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) output_kernel_bf16(Args a) {
-  using M = Mfma<bf16>;
-  typedef bf16x8 frag;
+template <typename T, int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) output_kernel_h(Args a) {
+  using M = Mfma<T>;
+  typedef typename M::frag frag;
   constexpr int NT = D / 16, KS_D = D / 32, KS_C = 2, NV = D / 32;
   constexpr int TPW = (NT + 3) / 4;  // value tiles per wave
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  OutSmemB<D> &sm = *reinterpret_cast<OutSmemB<D> *>(smem_raw);
+  OutSmemB<T, D> &sm = *reinterpret_cast<OutSmemB<T, D> *>(smem_raw);
 
   const int H = a.H;
   const int f = (int)(blockIdx.x / H), h = (int)(blockIdx.x % H);
@@ -232,8 +232,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) o
 
   // this wave's value tiles: chunk-start state and new-value fragments,
   // issued first so their latency overlaps the q/k staging
-  const bf16 *hf = (const bf16 *)a.Hf + ch * (int64_t)(D * D);
-  const bf16 *nfp = (const bf16 *)a.Nf + ch * (int64_t)(64 * D);
+  const T *hf = (const T *)a.Hf + ch * (int64_t)(D * D);
+  const T *nfp = (const T *)a.Nf + ch * (int64_t)(64 * D);
   frag hfr[TPW][KS_D], nfr[TPW][KS_C];
 #pragma unroll
   for (int x = 0; x < TPW; ++x) {
@@ -253,9 +253,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) o
     const bool valid = t < len;
     const int qh = h / (H / a.hq), kh = h / (H / a.hk);
     frag qn[NV], kn[NV];
-    load_norm_row_bf16<D>((const bf16 *)a.q + ((bos + t) * a.hq + qh) * D, p, valid,
+    load_norm_row16<T, D>((const T *)a.q + ((bos + t) * a.hq + qh) * D, p, valid,
                           a.l2norm != 0, qn);
-    load_norm_row_bf16<D>((const bf16 *)a.k + ((bos + t) * a.hk + kh) * D, p, valid,
+    load_norm_row16<T, D>((const T *)a.k + ((bos + t) * a.hk + kh) * D, p, valid,
                           a.l2norm != 0, kn);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -289,7 +289,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) o
         const int j = 16 * jt + 4 * g + r;
         const float pv = (j <= t) ? acc[r] * gexp(sm.Gs[t] - sm.Gs[j]) : 0.f;
         const int s = 4 * jt + r;
-        pf[s / 8][s % 8] = (bf16)pv;
+        pf[s / 8][s % 8] = (T)pv;
       }
     }
   }
@@ -299,7 +299,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) o
   lds_sync();
 
   // ---- O^T = S^T (diag(exp G) Q)^T + N^T P^T for this wave's value tiles ----
-  bf16 *out = (bf16 *)a.out;
+  T *out = (T *)a.out;
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     frag qf[KS_D];
@@ -324,36 +324,41 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) o
           acc = M::mma(nfr[x][kt], sm.kp.Pf[tt][kt][lane], acc);
       // acc[r] = O[t][16 jv + 4g + r]
       if (t < len) {
-        bf16x4 o4;
+        typename M::half o4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o4[r] = (bf16)(a.scale * acc[r]);
-        *reinterpret_cast<bf16x4 *>(out + ((bos + t) * H + h) * D + 16 * jv + 4 * g) = o4;
+        for (int r = 0; r < 4; ++r) o4[r] = (T)(a.scale * acc[r]);
+        *reinterpret_cast<typename M::half *>(out + ((bos + t) * H + h) * D + 16 * jv + 4 * g) = o4;
       }
     }
   }
 }
 
-template <int D>
-static hipError_t launch_output_bf16(const Args &a, hipStream_t s) {
-  const size_t smem = sizeof(OutSmemB<D>);
+template <typename T, int D>
+static hipError_t launch_output_h(const Args &a, hipStream_t s) {
+  const size_t smem = sizeof(OutSmemB<T, D>);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)output_kernel_bf16<D>,
+    hipError_t e = hipFuncSetAttribute((const void *)output_kernel_h<T, D>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t blocks = a.cap * a.H;
   if (blocks == 0) return hipSuccess;
-  output_kernel_bf16<D><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
+  output_kernel_h<T, D><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_output(const Args &a, hipStream_t s) {
   if (a.dtype == GDN_BF16) {
-    if (a.D == 128) return launch_output_bf16<128>(a, s);
-    if (a.D == 64) return launch_output_bf16<64>(a, s);
-    return launch_output_bf16<32>(a, s);
+    if (a.D == 128) return launch_output_h<bf16, 128>(a, s);
+    if (a.D == 64) return launch_output_h<bf16, 64>(a, s);
+    return launch_output_h<bf16, 32>(a, s);
+  }
+  if (a.dtype == GDN_F16) {
+    if (a.D == 128) return launch_output_h<f16, 128>(a, s);
+    if (a.D == 64) return launch_output_h<f16, 64>(a, s);
+    return launch_output_h<f16, 32>(a, s);
   }
   if (a.D == 128) return launch_output_t<float, 128>(a, s);
   if (a.D == 64) return launch_output_t<float, 64>(a, s);

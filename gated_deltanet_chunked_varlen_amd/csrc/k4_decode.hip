@@ -184,6 +184,11 @@ static hipError_t launch_decode_t(const Args &a, hipStream_t s) {
 }
 
 hipError_t launch_decode(const Args &a, hipStream_t s) {
+  if (a.dtype == GDN_F16) {
+    if (a.D == 128) return launch_decode_t<f16, 128>(a, s);
+    if (a.D == 64) return launch_decode_t<f16, 64>(a, s);
+    return launch_decode_t<f16, 32>(a, s);
+  }
   if (a.dtype == GDN_BF16) {
     if (a.D == 128) return launch_decode_t<bf16, 128>(a, s);
     if (a.D == 64) return launch_decode_t<bf16, 64>(a, s);

@@ -52,6 +52,12 @@ def _round_bf16_inplace(x: np.ndarray) -> np.ndarray:
     return x
 
 
+def round_f16(x: np.ndarray) -> np.ndarray:
+    """fp32 -> nearest-even IEEE half, returned as fp32 holding the fp16
+    values (numpy's conversion rounds to nearest even)."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """fp32 -> nearest-even bf16, returned as a new fp32 array holding the
     bf16 values (finite inputs)."""
@@ -102,7 +108,7 @@ def _unit_rows(x: np.ndarray) -> np.ndarray:
 @dataclass
 class Workload:
     """One call's inputs.  Arrays are fp32 holding values exactly
-    representable in ``dtype`` (``"bf16"`` or ``"f32"``)."""
+    representable in ``dtype`` (``"bf16"``, ``"f16"`` or ``"f32"``)."""
     name: str
     dtype: str
     cu_seqlens: np.ndarray                  # [N+1] int32 or int64
@@ -188,9 +194,13 @@ def make(seed: int, lengths, hq: int, hk: int, hv: int, D: int,
         sidx = _gen(kids[7]).permutation(pool_size)[:len(lengths)].astype(np.int32)
     if init_state is not None and init_dtype == "bf16":
         init_state = _round_bf16_inplace(init_state)
+    if init_state is not None and init_dtype == "f16":
+        init_state = round_f16(init_state)
     if dtype == "bf16":
         q, k, v = (_round_bf16_inplace(q), _round_bf16_inplace(k),
                    _round_bf16_inplace(v))
+    elif dtype == "f16":
+        q, k, v = round_f16(q), round_f16(k), round_f16(v)
     cu = _cu(lengths, cu_dtype)
     ccs = None
     if checkpoint_every > 0:

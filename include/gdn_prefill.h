@@ -70,7 +70,9 @@ typedef enum { GDN_I32 = 0, GDN_I64 = 1 } gdn_itype;
  *
  * Shapes, all row-major and contiguous unless strides are given:
  *   q [T, num_q_heads, D], k [T, num_k_heads, D], v [T, num_v_heads, D],
- *   qkv_dtype F32 or BF16 (F16 is rejected with GDN_ERR_DTYPE for now).
+ *   qkv_dtype F32, BF16 or F16 (gitcode, section "覆盖的公共输入域", names
+ *   FP16 and BF16 inputs).  Intermediates are kept in the input type for BF16
+ *   and F16 and in fp32 for F32; accumulation is always fp32.
  *   H = num_sab_heads = max(num_q_heads, num_v_heads); legal head sharing:
  *   (hq == hk and hv % hq == 0) or (hk == hv and hq % hk == 0); sab head h
  *   reads q head h / (H / hq), k head h / (H / hk), v head h / (H / hv).

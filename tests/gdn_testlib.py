@@ -2,7 +2,10 @@
 C ABI binding) and through the CPU oracle, and compare.
 
 Tolerances (relative L2 over each whole tensor, fp64): 1e-4 for fp32 inputs,
-2e-2 for bf16 inputs with fp32 accumulation.
+2e-2 for bf16 inputs with fp32 accumulation, and for fp16 inputs the bf16 bar
+scaled by the ratio of the two formats' unit roundoffs (2^-11 / 2^-8): the
+error comes from rounding the stored 16-bit intermediates, which scales with
+the unit roundoff.
 """
 from __future__ import annotations
 
@@ -10,7 +13,7 @@ import numpy as np
 
 from oracle import oracle
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2 / 8}
 
 
 def rel_l2(x, ref):
@@ -58,7 +61,7 @@ def _torch():
 
 def to_device(wl, device="cuda"):
     torch = _torch()
-    qdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    qdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[wl.dtype]
     sdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
     t = lambda a, dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dt)
     dev = dict(

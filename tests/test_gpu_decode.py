@@ -39,6 +39,7 @@ def _dec(seed, n, dtype="bf16", hq=4, hk=4, hv=4, D=128, **kw):
 
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("bf16", 32),
+                                     ("f16", 128), ("f16", 64),
                                      ("f32", 128), ("f32", 64), ("f32", 32)])
 def test_decode_dtype_and_head_size(dtype, D):
     wl = _dec(41, 37, dtype=dtype, D=D)

@@ -121,6 +121,7 @@ def _small(seed, lengths, dtype="bf16", hq=2, hk=2, hv=2, D=128, **kw):
 
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("bf16", 32),
+                                     ("f16", 128), ("f16", 64), ("f16", 32),
                                      ("f32", 128), ("f32", 64), ("f32", 32)])
 def test_dtype_and_head_size(dtype, D):
     wl = _small(11, [200, 64, 0, 65, 3], dtype=dtype, D=D, init="seq")
@@ -238,6 +239,16 @@ def test_status_checkpoint_starts_mismatch():
     wl.checkpoint_cu_starts[1] += 1                         # inconsistent
     gpu = tl.run_gpu(wl, status=True)
     assert gpu["status"] & 2
+
+
+def test_f16_two_by_2048_pool_f16_states():
+    # fp16 inputs with fp16 pool states at the 2 x 2048, 16-head shape
+    wl = W.make(33, [2048, 2048], 16, 16, 16, 128, "f16", l2norm_in_kernel=True,
+                init="pool", pool_size=4, init_dtype="f16", in_place_pool=True)
+    wl.initial_state_dtype = "f16"
+    gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] == 0
+    _check(wl, gpu, tl.run_oracle(wl))
 
 
 def test_many_sequences_chunk_table_path():

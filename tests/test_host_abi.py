@@ -116,7 +116,6 @@ def test_validate_ok_and_workspace():
     (dict(N=2, cu=False), "GDN_ERR_SHAPE"),
     (dict(hq=4, hk=2, hv=4), "GDN_ERR_HEAD_RATIO"),
     (dict(hq=4, hk=4, hv=6), "GDN_ERR_HEAD_RATIO"),
-    (dict(dtype=2), "GDN_ERR_DTYPE"),
     (dict(dtype=7), "GDN_ERR_DTYPE"),
     (dict(extra=dict(q=None)), "GDN_ERR_NULL"),
     (dict(extra=dict(checkpoint_every_n_tokens=100,
@@ -142,6 +141,7 @@ def test_validate_accepts_legal_variants():
     assert _validate(_params(T=100, N=4, extra=dict(max_seqlen=25))) == 0
     assert _validate(_params(T=0, N=3)) == 0                    # empty batch
     assert _validate(_params(dtype=nat.GDN_F32, D=32)) == 0
+    assert _validate(_params(dtype=nat.GDN_F16, D=64)) == 0     # fp16 inputs
 
 
 def test_validate_strides():
@@ -181,7 +181,7 @@ def test_validate_decode_ok():
     (dict(T=8, N=8, cu=True), "GDN_ERR_SHAPE"),           # no cu_seqlens
     (dict(T=8, N=8, cu=False, D=48), "GDN_ERR_SHAPE"),
     (dict(T=8, N=8, cu=False, hq=4, hk=2, hv=4), "GDN_ERR_HEAD_RATIO"),
-    (dict(T=8, N=8, cu=False, dtype=2), "GDN_ERR_DTYPE"),
+    (dict(T=8, N=8, cu=False, dtype=3), "GDN_ERR_DTYPE"),
     (dict(T=8, N=8, cu=False, extra=dict(checkpoint_every_n_tokens=64)), "GDN_ERR_CHECKPOINT"),
     (dict(T=8, N=8, cu=False, extra=dict(output_final_state=1)), "GDN_ERR_STATE"),
     (dict(T=8, N=8, cu=False, extra=dict(k=None)), "GDN_ERR_NULL"),
