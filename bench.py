@@ -57,7 +57,7 @@ def per_token_head_bytes(wl, phase):
     Shared q/k/v heads are counted once per source head.
     """
     D, H = wl.D, wl.H
-    e = 2 if wl.dtype == "bf16" else 4
+    e = 4 if wl.dtype == "f32" else 2
     hq, hk, hv = wl.q.shape[1], wl.k.shape[1], wl.v.shape[1]
     qf, kf, vf = hq / H, hk / H, hv / H
     st = D * D * e / 64.0          # chunk-start state per token
@@ -347,7 +347,7 @@ def main():
     tokens_per_s = T * K / (ms_total / 1e3)
     flops = T * H * FLOPS_PER_TOKEN_HEAD(D)
     tflops = flops / (ms_step / 1e3) / 1e12
-    peak_mm = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    peak_mm = FP32_PEAK_TFLOPS if wl.dtype == "f32" else BF16_PEAK_TFLOPS   # fp16 peak = bf16 peak
     bytes_launch = per_token_head_bytes(wl, dom) * T * H
     achieved = bytes_launch / (dom_ms / 1e3) / 1e9
     traffic = load_traffic(dom, wl.name)
