@@ -2,7 +2,7 @@
 """Benchmark of the varlen chunked Gated Delta Rule prefill on one MI355X.
 
 A step is one full ``gdn_prefill`` call (chunk-index build where the batch
-needs it, intra-chunk pass, state pass, output pass, all heads) over one
+needs it, intra-chunk pass, state pass with the output, all heads) over one
 batch of seeded synthetic input already resident in HBM; outputs and
 workspace are allocated once.  The
 default workload is 2 sequences x 2048 tokens, 16 heads, head size 128, bf16
@@ -49,17 +49,29 @@ def per_token_head_bytes(wl, phase):
     """Algorithmic HBM bytes per (token, sab head) of each phase (fp32 gates,
     q/k/v/o and intermediates in the compute dtype of width e).
 
-    intra : reads k, v, g, beta; writes W, Ktilde, U (64 x D each per
-            chunk-head) and the 64 cumulative log gates
-    state : reads W, Ktilde, U, G_last; writes the chunk-start state
-            (D x D per chunk-head) and the new values N (64 x D)
-    output: reads q, k, chunk-start state, N, G; writes o
+    16-bit inputs (the state pass forms the output itself):
+      intra : reads q, k, v, g, beta; writes W, Ktilde, U and the q fragments
+              (64 x D each per chunk-head), the masked Q K^T (64 x 64) and the
+              64 cumulative log gates
+      state : reads W, Ktilde, U, the q fragments, Q K^T and the gates;
+              writes o
+    fp32 inputs (separate output pass):
+      intra : reads k, v, g, beta; writes W, Ktilde, U and the gates
+      state : reads W, Ktilde, U, G_last; writes the chunk-start state
+              (D x D per chunk-head) and the new values N (64 x D)
+      output: reads q, k, chunk-start state, N, G; writes o
     Shared q/k/v heads are counted once per source head.
     """
     D, H = wl.D, wl.H
     e = 4 if wl.dtype == "f32" else 2
     hq, hk, hv = wl.q.shape[1], wl.k.shape[1], wl.v.shape[1]
     qf, kf, vf = hq / H, hk / H, hv / H
+    if wl.dtype != "f32":
+        if phase == "intra":
+            return (qf + kf + vf) * D * e + 8 + 4 * D * e + 64 * e + 4
+        if phase == "state":
+            return 4 * D * e + 64 * e + 4 + D * e
+        return 0.0
     st = D * D * e / 64.0          # chunk-start state per token
     if phase == "intra":
         return (kf + vf) * D * e + 8 + 3 * D * e + 4

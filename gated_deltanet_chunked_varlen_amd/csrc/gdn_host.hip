@@ -35,7 +35,8 @@ bool valid_state_dtype(int d) { return d == GDN_F32 || d == GDN_BF16 || d == GDN
 bool valid_itype(int t) { return t == GDN_I32 || t == GDN_I64; }
 
 struct Layout {
-  size_t chunk_idx, chunk_tok, cu_chunks, seq_bos, n_chunks, Wf, Kf, Uf, Hf, Nf, Gw, total;
+  size_t chunk_idx, chunk_tok, cu_chunks, seq_bos, n_chunks, Wf, Kf, Uf, Hf, Nf, Qf, Pf, Gw, total;
+  bool fuse;
 };
 
 Layout plan(const gdn_prefill_params *p) {
@@ -54,8 +55,16 @@ Layout plan(const gdn_prefill_params *p) {
   L.Wf = take(blocks * 64 * D * es);
   L.Kf = take(blocks * 64 * D * es);
   L.Uf = take(blocks * 64 * D * es);
-  L.Nf = take(blocks * 64 * D * es);
-  L.Hf = take(blocks * D * D * es);
+  // 16-bit inputs: the state pass forms the output itself and needs the q and
+  // P fragments instead of chunk-start states and N in memory
+  L.fuse = p->qkv_dtype != GDN_F32;
+  if (L.fuse) {
+    L.Qf = take(blocks * 64 * D * es);
+    L.Pf = take(blocks * 64 * 64 * es);
+  } else {
+    L.Nf = take(blocks * 64 * D * es);
+    L.Hf = take(blocks * D * D * es);
+  }
   L.Gw = take(blocks * 64 * sizeof(float));
   L.total = off;
   return L;
@@ -256,8 +265,14 @@ static void fill_args(const gdn_prefill_params *p, const Layout *L, int num_cus,
     a.Wf = ws + L->Wf;
     a.Kf = ws + L->Kf;
     a.Uf = ws + L->Uf;
-    a.Hf = ws + L->Hf;
-    a.Nf = ws + L->Nf;
+    if (L->fuse) {
+      a.Qf = ws + L->Qf;
+      a.Pf = ws + L->Pf;
+      a.fuse = 1;
+    } else {
+      a.Hf = ws + L->Hf;
+      a.Nf = ws + L->Nf;
+    }
     a.Gw = (float *)(ws + L->Gw);
   }
   a.cap = gdn_max_chunks(p->total_tokens, p->num_seqs);
@@ -315,9 +330,15 @@ static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess && a.cap > 0) e = launch_intra(a, s);
   if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess) e = launch_state(a, s);
-  if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess && a.cap > 0) e = launch_output(a, s);
+  if (a.fuse) {
+    // state and output in one pass; the output phase is empty
+    if (e == hipSuccess) e = launch_state_output(a, s);
+    if (e == hipSuccess) e = mark(3);
+  } else {
+    if (e == hipSuccess) e = launch_state(a, s);
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess && a.cap > 0) e = launch_output(a, s);
+  }
   if (e == hipSuccess) e = mark(4);
   return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }

@@ -39,6 +39,10 @@ struct Args {
   int64_t cap;
   // intermediates
   void *Wf, *Kf, *Uf, *Hf, *Nf;
+  // operands of the output products when the state pass produces the output
+  // itself (fuse != 0): normalised q and masked Q K^T as fragments
+  void *Qf, *Pf;
+  int32_t fuse;
   float *Gw;
   // states
   const void *init;
@@ -111,20 +115,28 @@ __device__ __forceinline__ void chunk_geometry(const Args &a, int f, int lane, b
   }
 }
 
-// First flat chunk, chunk count and length of sequence seq, for the calling
-// wave.
+// First flat chunk, chunk count, length and first token of sequence seq, for
+// the calling wave.
 __device__ __forceinline__ void seq_geometry(const Args &a, int seq, int lane, int &f0, int &nc,
-                                             int &len) {
+                                             int &len, int &bos) {
   if (a.direct) {
     const SeqLane s = seq_lane(a.cu, a.cu_type, a.N, a.T, lane);
     f0 = __shfl(s.cc0, seq);
     nc = __shfl(s.cc1, seq) - f0;
     len = __shfl(s.len, seq);
+    bos = __shfl(s.bos, seq);
   } else {
     f0 = a.cu_chunks[seq];
     nc = min(a.cu_chunks[seq + 1], a.n_chunks[0]) - f0;
     len = a.seq_bos[seq + 1] - a.seq_bos[seq];
+    bos = a.seq_bos[seq];
   }
+}
+
+__device__ __forceinline__ void seq_geometry(const Args &a, int seq, int lane, int &f0, int &nc,
+                                             int &len) {
+  int bos;
+  seq_geometry(a, seq, lane, f0, nc, len, bos);
 }
 #endif
 
@@ -139,5 +151,6 @@ hipError_t launch_intra(const Args &a, hipStream_t s);
 hipError_t launch_state(const Args &a, hipStream_t s);
 hipError_t launch_output(const Args &a, hipStream_t s);
 hipError_t launch_decode(const Args &a, hipStream_t s);
+hipError_t launch_state_output(const Args &a, hipStream_t s);
 
 }  // namespace gdn

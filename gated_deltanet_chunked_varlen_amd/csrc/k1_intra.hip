@@ -339,6 +339,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
                           a.l2norm != 0, kn);
 #pragma unroll
     for (int i = 0; i < NV; ++i) *reinterpret_cast<frag *>(&KV[lt][32 * i + 8 * lp]) = kn[i];
+    if (a.fuse) {
+      // q rows (normalised) go to the A/T buffer until A is formed: row t at
+      // byte 272 t, below the G / beta columns (bytes 256 .. 263 of the row)
+      const int qh = h / (H / a.hq);
+      frag qn[NV];
+      load_norm_row16<T, D>((const T *)a.q + ((bos + lt) * a.hq + qh) * D, lp, valid,
+                            a.l2norm != 0, qn);
+      T *qrow = reinterpret_cast<T *>(&AT[lt][0]);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) *reinterpret_cast<frag *>(qrow + 32 * i + 8 * lp) = qn[i];
+    }
   }
   if (wave == 0) {
     const int t = lane;
@@ -359,6 +370,51 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
     a.Gw[ch * kChunk + t] = la;
   }
   lds_sync();
+
+  if (a.fuse) {
+    // ---- operands of the output products, for the fused state pass --------
+    // Pf [tt][kt]: P[16 tt + c][pi(g, 8 kt + e)] with P = (Q K^T) masked to
+    //   j <= t and scaled by exp(G_t - G_j) (P^T = K Q^T leaves P rows in the
+    //   operand order); Qf [tt][kt]: q[16 tt + c][pi(g, 8 kt + e)].
+    const int tt = wave;
+    const T(*QR)[136] = reinterpret_cast<const T(*)[136]>(&AT[0][0]);
+    T *pf_out = (T *)a.Pf + ch * (int64_t)(64 * 64);
+    T *qf_out = (T *)a.Qf + ch * (int64_t)(64 * D);
+    frag pf[KS_C];
+    const int t = 16 * tt + c;
+    const float gt = AT[t][64];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (jt <= tt) {
+#pragma unroll
+        for (int kt = 0; kt < KS_D; ++kt) {
+          const int k0 = kt * 32 + g * 8;
+          const frag fa = *reinterpret_cast<const frag *>(&KV[16 * jt + c][k0]);
+          const frag fb = *reinterpret_cast<const frag *>(&QR[16 * tt + c][k0]);
+          acc = M::mma(fa, fb, acc);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * jt + 4 * g + r;
+        const float pv = (j <= t) ? acc[r] * gexp(gt - AT[j][64]) : 0.f;
+        const int sl = 4 * jt + r;
+        pf[sl / 8][sl % 8] = (T)pv;
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < KS_C; ++kt)
+      *reinterpret_cast<frag *>(pf_out + (((int64_t)tt * KS_C + kt) * 64 + lane) * 8) = pf[kt];
+#pragma unroll
+    for (int kt = 0; kt < KS_D; ++kt) {
+      frag qf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[e] = QR[t][pi_idx(g, kt * 8 + e)];
+      *reinterpret_cast<frag *>(qf_out + (((int64_t)tt * KS_D + kt) * 64 + lane) * 8) = qf;
+    }
+    lds_sync();  // q is consumed: A may overwrite the buffer
+  }
 
   // ---- A = strictly-lower(beta_t exp(G_t - G_j) k_t.k_j) ------------------
   {

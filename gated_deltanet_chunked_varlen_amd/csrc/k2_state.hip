@@ -15,11 +15,12 @@
 // (sequence, sab head, 16-column tile): its 16 x D slice of S lives in
 // registers in matrix-core result layout for the whole sequence, and the
 // result registers of each product are the next product's operand (see the
-// register-reuse note in gdn_common.h).  Per chunk it also stores the
-// chunk-start state and N for the output pass, writes checkpoints (gitcode
-// "FlashInfer GDN Prefill 完全指南", section "中间状态检查点") and, at the end,
-// the final state into output_state (row state_indices[i] for a pool,
-// section "状态池").
+// register-reuse note in gdn_common.h).  Per chunk it also hands the
+// chunk-start state and N to the output (stored for the fp32 output pass, or
+// passed through LDS to the output waves of the fused 16-bit pass below),
+// writes checkpoints (gitcode "FlashInfer GDN Prefill 完全指南", section
+// "中间状态检查点") and, at the end, the final state into output_state (row
+// state_indices[i] for a pool, section "状态池").
 //
 // Workgroup -> tile mapping: consecutive workgroup ids are dealt round-robin
 // to the 8 XCDs, so the NT tiles of one (sequence, head) get ids equal mod 8
@@ -121,10 +122,14 @@ struct LdsOps {
 };
 
 // One chunk of the state recurrence for one lane's share of a 16-column tile.
+// With xb non-null (the fused state/output pass) the chunk-start state and
+// N fragments go to that LDS buffer instead of the workspace: KS_D state
+// fragments, then KS_C new-value fragments, 64 lanes each.
 template <typename T, int D, typename Ops>
 __device__ __forceinline__ void chunk_step(const Args &a, const Ops &op,
                                            float (&S)[D / 16][4], int64_t ch, int jv,
-                                           int lane) {
+                                           int lane,
+                                           typename Mfma<T>::frag *xb = nullptr) {
   using M = Mfma<T>;
   using Ge = Geo<T, D>;
   typedef typename M::frag frag;
@@ -148,7 +153,10 @@ __device__ __forceinline__ void chunk_step(const Args &a, const Ops &op,
 #pragma unroll
   for (int kt = 0; kt < KS_D; ++kt) sb[kt] = M::pack(Sflat + kt * KPL);
   // chunk-start state, stored for the output pass
-  {
+  if (xb) {
+#pragma unroll
+    for (int kt = 0; kt < KS_D; ++kt) xb[kt * 64 + lane] = sb[kt];
+  } else {
     T *hf = (T *)a.Hf + ch * Ge::H_ELEMS + (int64_t)jv * KS_D * 64 * KPL;
 #pragma unroll
     for (int kt = 0; kt < KS_D; ++kt)
@@ -185,7 +193,8 @@ __device__ __forceinline__ void chunk_step(const Args &a, const Ops &op,
 #pragma unroll
     for (int kt = 0; kt < KS_C; ++kt) {
       nf[kt] = M::pack(accf + kt * KPL);
-      *reinterpret_cast<frag *>(nfp + ((int64_t)kt * 64 + lane) * KPL) = nf[kt];
+      if (xb) xb[(KS_D + kt) * 64 + lane] = nf[kt];
+      else *reinterpret_cast<frag *>(nfp + ((int64_t)kt * 64 + lane) * KPL) = nf[kt];
     }
   }
   // S' = exp(G_last) S + Ktilde^T N
@@ -318,93 +327,174 @@ __global__ void __launch_bounds__(64) state_kernel(Args a) {
 }
 
 
-// Loader waves per workgroup of the bf16 state pass.
-#ifndef GDN_STATE_NLW
-#define GDN_STATE_NLW 6
-#endif
-// loader waves that store one chunk into LDS together
-#ifndef GDN_STATE_TEAM
-#define GDN_STATE_TEAM 3
-#endif
+// ===========================================================================
+// Fused state and output pass (16-bit inputs).
+//
+// 0539edu "GDN与线性注意力GPU并行实现", section 3.3, splits a chunk's output
+// into what it reads from its start state and what it wrote itself; the
+// state pass holds the first (S in registers) and produces the second's
+// operand (N), so the output can be formed there instead of in a separate
+// pass that would read both back from memory:
+//
+//   O = scale * ( diag(exp(G)) Q S + P N ),   P = (Q K^T) masked, from K1
+//
+// A workgroup owns one 16-column tile of one (sequence, head):
+//   wave 0      compute: the recurrence; per chunk it reads W / Ktilde / U
+//               from LDS and leaves the chunk's start-state and N fragments
+//               in an LDS buffer;
+//   OUTW waves  output: one chunk behind, O^T = S^T (diag(exp G) Q)^T +
+//               N^T P^T for the tile's 16 columns, split over token tiles,
+//               four consecutive columns per lane and 8-byte stores (only
+//               rows inside the sequence);
+//   NLW waves   loaders, in teams of TEAM waves (team j owns chunks
+//               c = j mod NLW / TEAM): per chunk they fetch W, Ktilde, the
+//               tile's U (compute part, two-slot ring) and q fragments, P
+//               fragments and the gate row (output part, three-slot ring),
+//               and store them into LDS together.
+// Step st (one LDS-only barrier each): loaders store chunk st, the compute
+// wave works on chunk st - 1, the output wave on chunk st - 2.
+// ===========================================================================
+template <typename T, int D>
+struct OutSlotGeo {
+  static constexpr int Q_BYTES = 64 * D * 2;
+  static constexpr int P_OFF = Q_BYTES;
+  static constexpr int P_BYTES = 64 * 64 * 2;
+  static constexpr int G_OFF = P_OFF + P_BYTES;
+  static constexpr int BYTES = G_OFF + 64 * 4;
+  static constexpr int NV_Q = Q_BYTES / (64 * 16);
+  static constexpr int NV_P = P_BYTES / (64 * 16);
+};
 
-// One chunk's operands split over the TEAM loader waves of a team: wave part p
-// of the team holds the 16-byte pieces i = p (mod TEAM) of the chunk's LDS
-// slot, so storing a chunk into LDS takes TEAM waves in parallel.
-template <typename T, int D, int NCW, int TEAM>
-struct TeamLoader {
-  using SG = SlotGeo<T, D, NCW>;
-  static constexpr int64_t BLK = Geo<T, D>::W_ELEMS * sizeof(T) / 16;  // u32x4 per block
-  static constexpr int PPW = (SG::NV + TEAM - 1) / TEAM;              // pieces per wave
+template <typename T, int D, int TEAM>
+struct FusedLoader {
+  using CS = SlotGeo<T, D, 1>;
+  using OS = OutSlotGeo<T, D>;
+  static constexpr int64_t BLK = Geo<T, D>::W_ELEMS * sizeof(T) / 16;   // u32x4 per 64 x D block
+  static constexpr int64_t PBLK = 64 * 64 * sizeof(T) / 16;              // u32x4 per P block
+  static constexpr int NV = CS::NV + OS::NV_Q + OS::NV_P;                // pieces per chunk
+  static constexpr int PPW = (NV + TEAM - 1) / TEAM;
   u32x4 v[PPW];
-  float glog;
+  float gv;
   int64_t uoff;
   int lane, part;
 
   __device__ __forceinline__ void init(int jg, int ln, int pt) {
-    uoff = (int64_t)jg * NCW * (SG::U_TILE_BYTES / 16);
+    uoff = (int64_t)jg * (CS::U_TILE_BYTES / 16);
     lane = ln;
     part = pt;
   }
+  // piece i of a chunk: W, Ktilde, U tile (compute slot), q, P (output slot)
   __device__ __forceinline__ void issue(const Args &a, int64_t ch) {
     const u32x4 *__restrict__ wf = reinterpret_cast<const u32x4 *>(a.Wf) + ch * BLK + lane;
     const u32x4 *__restrict__ kf = reinterpret_cast<const u32x4 *>(a.Kf) + ch * BLK + lane;
     const u32x4 *__restrict__ uf = reinterpret_cast<const u32x4 *>(a.Uf) + ch * BLK + uoff + lane;
+    const u32x4 *__restrict__ qf = reinterpret_cast<const u32x4 *>(a.Qf) + ch * BLK + lane;
+    const u32x4 *__restrict__ pf = reinterpret_cast<const u32x4 *>(a.Pf) + ch * PBLK + lane;
 #pragma unroll
     for (int m = 0; m < PPW; ++m) {
       const int i = part + TEAM * m;
-      if (SG::NV % TEAM == 0 || i < SG::NV) {
-        const u32x4 *src = i < SG::NV_W ? wf + (int64_t)i * 64
-                         : i < 2 * SG::NV_W ? kf + (int64_t)(i - SG::NV_W) * 64
-                                            : uf + (int64_t)(i - 2 * SG::NV_W) * 64;
+      if (NV % TEAM == 0 || i < NV) {
+        const u32x4 *src;
+        if (i < CS::NV_W) src = wf + (int64_t)i * 64;
+        else if (i < 2 * CS::NV_W) src = kf + (int64_t)(i - CS::NV_W) * 64;
+        else if (i < CS::NV) src = uf + (int64_t)(i - 2 * CS::NV_W) * 64;
+        else if (i < CS::NV + OS::NV_Q) src = qf + (int64_t)(i - CS::NV) * 64;
+        else src = pf + (int64_t)(i - CS::NV - OS::NV_Q) * 64;
         v[m] = *src;
       }
     }
-    if (part == 0) glog = a.Gw[ch * kChunk + (kChunk - 1)];
+    if (part == 0) gv = a.Gw[ch * kChunk + lane];
   }
-  __device__ __forceinline__ void drop(unsigned char *slot) const {
-    u32x4 *dst = reinterpret_cast<u32x4 *>(slot) + lane;
+  __device__ __forceinline__ void drop(unsigned char *cslot, unsigned char *oslot) const {
+    u32x4 *cdst = reinterpret_cast<u32x4 *>(cslot) + lane;
+    u32x4 *odst = reinterpret_cast<u32x4 *>(oslot) + lane;
 #pragma unroll
     for (int m = 0; m < PPW; ++m) {
       const int i = part + TEAM * m;
-      if (SG::NV % TEAM == 0 || i < SG::NV) dst[i * 64] = v[m];
+      if (NV % TEAM == 0 || i < NV) {
+        if (i < CS::NV) cdst[i * 64] = v[m];
+        else odst[(i - CS::NV) * 64] = v[m];
+      }
     }
-    if (part == 0 && lane == 0) *reinterpret_cast<float *>(slot + SG::G_OFF) = glog;
+    if (part == 0) {
+      reinterpret_cast<float *>(oslot + OS::G_OFF)[lane] = gv;
+      if (lane == kChunk - 1) *reinterpret_cast<float *>(cslot + CS::G_OFF) = gv;
+    }
   }
 };
 
-// Producer/consumer variant (bf16).  A workgroup owns NCW adjacent 16-column
-// tiles of one (sequence, head): NCW compute waves run the recurrence, NLW
-// loader waves keep the operands of upcoming chunks in flight in their own
-// registers.  Loader w owns chunks c = w (mod NLW): it issues chunk c's loads
-// NLW steps ahead and drops the data into LDS slot c % 2 during step c, while
-// the compute waves work on chunk c - 1 from the other slot.  One LDS-only
-// barrier per step orders the two (a full barrier would also wait for the
-// loads in flight and undo the look-ahead).  The compute waves share every
-// W / Ktilde fragment they read.
-template <typename T, int D, int NCW, int NLW>
-__global__ void __launch_bounds__(64 * (NCW + NLW)) state_kernel_pipe(Args a) {
+// The output of one chunk for one 16-column tile (output wave).
+template <typename T, int D, int OUTW>
+__device__ __forceinline__ void output_step(const Args &a, const unsigned char *oslot,
+                                            const typename Mfma<T>::frag *xb, int jv,
+                                            int64_t tok0, int rows, int h, int lane, int ow) {
+  using M = Mfma<T>;
+  typedef typename M::frag frag;
+  using OS = OutSlotGeo<T, D>;
+  constexpr int KS_D = Geo<T, D>::KS_D, KS_C = Geo<T, D>::KS_C;
+  const int g = lane >> 4, c = lane & 15;
+  const frag *qf = reinterpret_cast<const frag *>(oslot);
+  const frag *pf = reinterpret_cast<const frag *>(oslot + OS::P_OFF);
+  const float *gs = reinterpret_cast<const float *>(oslot + OS::G_OFF);
+  frag sf[KS_D], nf[KS_C];
+#pragma unroll
+  for (int kt = 0; kt < KS_D; ++kt) sf[kt] = xb[kt * 64 + lane];
+#pragma unroll
+  for (int kt = 0; kt < KS_C; ++kt) nf[kt] = xb[(KS_D + kt) * 64 + lane];
+  T *out = (T *)a.out;
+  const int H = a.H;
+#pragma unroll
+  for (int i = 0; i < 4 / OUTW; ++i) {
+    // token tiles of output wave ow: all four, or {0, 3} / {1, 2} (equal work)
+    const int tt = OUTW == 1 ? i : (i == 0 ? ow : 3 - ow);
+    const int t = 16 * tt + c;  // this lane's output row
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < KS_D; ++kt) acc = M::mma(sf[kt], qf[(tt * KS_D + kt) * 64 + lane], acc);
+    const float gam = gexp(gs[t]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] *= gam;
+#pragma unroll
+    for (int kt = 0; kt < KS_C; ++kt)
+      if (kt * 2 <= tt)  // k-step's first token tile is not masked out
+        acc = M::mma(nf[kt], pf[(tt * KS_C + kt) * 64 + lane], acc);
+    // acc[r] = O[t][16 jv + 4g + r]
+    if (t < rows) {
+      typename M::half o4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o4[r] = (T)(a.scale * acc[r]);
+      *reinterpret_cast<typename M::half *>(out + ((tok0 + t) * H + h) * D + 16 * jv + 4 * g) = o4;
+    }
+  }
+}
+
+template <typename T, int D, int OUTW, int NLW, int TEAM>
+__global__ void __launch_bounds__(64 * (1 + OUTW + NLW)) state_output_kernel(Args a) {
   constexpr int NT = D / 16;
-  constexpr int NGRP = NT / NCW;
-  using SG = SlotGeo<T, D, NCW>;
-  __shared__ __align__(16) unsigned char slots[2][SG::BYTES];
+  using CS = SlotGeo<T, D, 1>;
+  using OS = OutSlotGeo<T, D>;
+  typedef typename Mfma<T>::frag frag;
+  constexpr int XB = Geo<T, D>::KS_D + Geo<T, D>::KS_C;  // fragments per chunk in xbuf
+  __shared__ __align__(16) unsigned char cslots[2][CS::BYTES];
+  __shared__ __align__(16) unsigned char oslots[3][OS::BYTES];
+  __shared__ frag xbuf[2][XB * 64];
 
   const int b = blockIdx.x;
-  const int jg = (b >> 3) % NGRP;
-  const int u = (b / (8 * NGRP)) * 8 + (b & 7);
+  const int jg = (b >> 3) % NT;
+  const int u = (b / (8 * NT)) * 8 + (b & 7);
   const int H = a.H;
   if (u >= a.N * H) return;
   const int seq = u / H, h = u % H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
 
-  int f0, nc, len;
-  seq_geometry(a, seq, lane, f0, nc, len);
+  int f0, nc, len, sbos;
+  seq_geometry(a, seq, lane, f0, nc, len, sbos);
   const int64_t ch0 = ws_index(f0, h, a.cap);
 
-  if (wave < NCW) {
-    // ---------------- compute wave: tile jv -------------------------------
-    const int jv = jg * NCW + wave;
-    const int vcol = 16 * jv + c;
+  if (wave == 0) {
+    // ---------------- compute wave ------------------------------------------
+    const int vcol = 16 * jg + c;
     int64_t row = seq;
     bool row_ok = true;
     if (a.sidx) {
@@ -414,12 +504,12 @@ __global__ void __launch_bounds__(64 * (NCW + NLW)) state_kernel_pipe(Args a) {
     float S[NT][4];
     read_state<D>(a, row_ok, row, h, vcol, g, S);
     const int64_t ck_base = a.ck_every > 0 ? ld_index(a.ck_cs, a.ck_cs_type, seq) : 0;
-    for (int st = 0; st <= nc; ++st) {
+    for (int st = 0; st <= nc + 1; ++st) {
       lds_sync();
-      if (st == 0) continue;
+      if (st == 0 || st > nc) continue;
       const int cc = st - 1;
-      const LdsOps<T, D, NCW> op{slots[cc & 1], lane, wave};
-      chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jv, lane);
+      const LdsOps<T, D, 1> op{cslots[cc & 1], lane, 0};
+      chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[cc & 1]);
       if (a.ck_every > 0) {
         const int done = (cc + 1) * kChunk;
         if (done <= len && done % a.ck_every == 0) {
@@ -431,26 +521,64 @@ __global__ void __launch_bounds__(64 * (NCW + NLW)) state_kernel_pipe(Args a) {
     }
     if (a.out_final && a.outst && row_ok)
       write_state<T, D>(a.outst, a.out_dtype, a.out_str, row, h, vcol, g, S);
+  } else if (wave <= OUTW) {
+    // ---------------- output waves: one chunk behind the compute wave --------
+    for (int st = 0; st <= nc + 1; ++st) {
+      lds_sync();
+      if (st < 2) continue;
+      const int oc = st - 2;
+      output_step<T, D, OUTW>(a, oslots[oc % 3], xbuf[oc & 1], jg,
+                              (int64_t)sbos + (int64_t)kChunk * oc, min(kChunk, len - kChunk * oc),
+                              h, lane, wave - 1);
+    }
   } else {
-    // ---------------- loader waves -----------------------------------------
-    // NLW / TEAM teams; team j owns chunks c = j (mod NLW / TEAM) and its
-    // TEAM waves load and store each of them together.  The loads stay in
-    // flight across the LDS-only barriers, so they have NLW / TEAM steps to
-    // arrive.
-    constexpr int NTEAM = NLW / GDN_STATE_TEAM;
-    static_assert(NLW % GDN_STATE_TEAM == 0, "loader waves split into whole teams");
-    const int lw = wave - NCW, team = lw / GDN_STATE_TEAM;
-    TeamLoader<T, D, NCW, GDN_STATE_TEAM> ld;
-    ld.init(jg, lane, lw % GDN_STATE_TEAM);
+    // ---------------- loader waves ------------------------------------------
+    constexpr int NTEAM = NLW / TEAM;
+    static_assert(NLW % TEAM == 0, "loader waves split into whole teams");
+    const int lw = wave - 1 - OUTW, team = lw / TEAM;
+    FusedLoader<T, D, TEAM> ld;
+    ld.init(jg, lane, lw % TEAM);
     if (team < nc) ld.issue(a, ch0 + (int64_t)team);
-    for (int st = 0; st <= nc; ++st) {
+    for (int st = 0; st <= nc + 1; ++st) {
       lds_sync();
       if (st < nc && st % NTEAM == team) {
-        ld.drop(slots[st & 1]);
+        ld.drop(cslots[st & 1], oslots[st % 3]);
         if (st + NTEAM < nc) ld.issue(a, ch0 + (int64_t)(st + NTEAM));
       }
     }
   }
+}
+
+#ifndef GDN_FUSED_OUTW
+#define GDN_FUSED_OUTW 2
+#endif
+#ifndef GDN_FUSED_NLW
+#define GDN_FUSED_NLW 5
+#endif
+#ifndef GDN_FUSED_TEAM
+#define GDN_FUSED_TEAM 5
+#endif
+
+template <typename T, int D>
+static hipError_t launch_state_output_t(const Args &a, hipStream_t s) {
+  constexpr int NT = D / 16, OUTW = GDN_FUSED_OUTW, NLW = GDN_FUSED_NLW, TEAM = GDN_FUSED_TEAM;
+  const int64_t units = (int64_t)a.N * a.H;
+  if (units == 0) return hipSuccess;
+  const int64_t blocks = ((units + 7) / 8) * 8 * NT;
+  state_output_kernel<T, D, OUTW, NLW, TEAM>
+      <<<dim3((unsigned)blocks), dim3(64 * (1 + OUTW + NLW)), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_output(const Args &a, hipStream_t s) {
+  if (a.dtype == GDN_F16) {
+    if (a.D == 128) return launch_state_output_t<f16, 128>(a, s);
+    if (a.D == 64) return launch_state_output_t<f16, 64>(a, s);
+    return launch_state_output_t<f16, 32>(a, s);
+  }
+  if (a.D == 128) return launch_state_output_t<bf16, 128>(a, s);
+  if (a.D == 64) return launch_state_output_t<bf16, 64>(a, s);
+  return launch_state_output_t<bf16, 32>(a, s);
 }
 
 template <typename T, int D>
@@ -464,41 +592,8 @@ static hipError_t launch_state_t(const Args &a, hipStream_t s) {
 }
 
 
-template <typename T, int D, int NCW, int NLW>
-static hipError_t launch_state_pipe_t(const Args &a, hipStream_t s) {
-  constexpr int NGRP = D / 16 / NCW;
-  const int64_t units = (int64_t)a.N * a.H;
-  if (units == 0) return hipSuccess;
-  const int64_t blocks = ((units + 7) / 8) * 8 * NGRP;
-  state_kernel_pipe<T, D, NCW, NLW><<<dim3((unsigned)blocks), dim3(64 * (NCW + NLW)), 0, s>>>(a);
-  return hipGetLastError();
-}
-
+// fp32 inputs (16-bit inputs take the fused state/output pass above)
 hipError_t launch_state(const Args &a, hipStream_t s) {
-  if (a.dtype == GDN_F16) {
-    constexpr int NLW = GDN_STATE_NLW;
-    const int64_t units = (int64_t)a.N * a.H;
-    const bool wide = units * (a.D / 16) > (int64_t)a.num_cus;
-    if (a.D == 128)
-      return wide ? launch_state_pipe_t<f16, 128, 2, NLW>(a, s) : launch_state_pipe_t<f16, 128, 1, NLW>(a, s);
-    if (a.D == 64)
-      return wide ? launch_state_pipe_t<f16, 64, 2, NLW>(a, s) : launch_state_pipe_t<f16, 64, 1, NLW>(a, s);
-    return wide ? launch_state_pipe_t<f16, 32, 2, NLW>(a, s) : launch_state_pipe_t<f16, 32, 1, NLW>(a, s);
-  }
-  if (a.dtype == GDN_BF16) {
-    constexpr int NLW = GDN_STATE_NLW;
-    // One compute wave (16 columns) per workgroup while the workgroups fit on
-    // the CUs at once: that halves each CU's LDS traffic per column.  With
-    // more (sequence, head) pairs than that, two compute waves per workgroup
-    // halve the number of workgroups instead.
-    const int64_t units = (int64_t)a.N * a.H;
-    const bool wide = units * (a.D / 16) > (int64_t)a.num_cus;
-    if (a.D == 128)
-      return wide ? launch_state_pipe_t<bf16, 128, 2, NLW>(a, s) : launch_state_pipe_t<bf16, 128, 1, NLW>(a, s);
-    if (a.D == 64)
-      return wide ? launch_state_pipe_t<bf16, 64, 2, NLW>(a, s) : launch_state_pipe_t<bf16, 64, 1, NLW>(a, s);
-    return wide ? launch_state_pipe_t<bf16, 32, 2, NLW>(a, s) : launch_state_pipe_t<bf16, 32, 1, NLW>(a, s);
-  }
   if (a.D == 128) return launch_state_t<float, 128>(a, s);
   if (a.D == 64) return launch_state_t<float, 64>(a, s);
   return launch_state_t<float, 32>(a, s);

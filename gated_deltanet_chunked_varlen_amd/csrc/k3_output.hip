@@ -1,4 +1,5 @@
-// k3_output.hip -- output pass.
+// k3_output.hip -- output pass for fp32 inputs.  (With 16-bit inputs the
+// fused state/output pass in k2_state.hip forms the output instead.)
 //
 // Every token reads the state after its own update (weigao.cc "GDN 与 Chunked
 // Prefill", section "块内 state 和块间 final state").  Inside a chunk that
@@ -191,175 +192,8 @@ static hipError_t launch_output_t(const Args &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// 16-bit (bf16 / fp16) variant.  The same products, computed transposed: O^T = S^T (diag(exp
-// G) Q)^T + N^T P^T.  The stored chunk-start state and new values are already
-// in the operand layout this needs, so every lane ends up holding four
-// consecutive output columns of one row and stores them as one 8-byte write;
-// there is no staging tile.  P's fragments reuse the k buffer once every wave
-// has finished reading k, so q, k/P and the gates take about 35 KB at
-// D = 128 and four workgroups share a CU.
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-struct OutSmemB {
-  static constexpr int LDQ = D + 8;
-  T Qs[64][LDQ];
-  union {
-    T Ks[64][LDQ];         // k rows, for P
-    typename Mfma<T>::frag Pf[4][2][64];      // P rows as operand fragments, after P
-  } kp;
-  float Gs[64];
-};
-
-template <typename T, int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) output_kernel_h(Args a) {
-  using M = Mfma<T>;
-  typedef typename M::frag frag;
-  constexpr int NT = D / 16, KS_D = D / 32, KS_C = 2, NV = D / 32;
-  constexpr int TPW = (NT + 3) / 4;  // value tiles per wave
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  OutSmemB<T, D> &sm = *reinterpret_cast<OutSmemB<T, D> *>(smem_raw);
-
-  const int H = a.H;
-  const int f = (int)(blockIdx.x / H), h = (int)(blockIdx.x % H);
-  const int64_t ch = ws_index(f, h, a.cap);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int tb, len;
-  chunk_geometry(a, f, lane, false, tb, len);
-  if (len <= 0) return;
-  const int64_t bos = tb;
-  const int g = lane >> 4, c = lane & 15;
-
-  // this wave's value tiles: chunk-start state and new-value fragments,
-  // issued first so their latency overlaps the q/k staging
-  const T *hf = (const T *)a.Hf + ch * (int64_t)(D * D);
-  const T *nfp = (const T *)a.Nf + ch * (int64_t)(64 * D);
-  frag hfr[TPW][KS_D], nfr[TPW][KS_C];
-#pragma unroll
-  for (int x = 0; x < TPW; ++x) {
-    const int jv = wave * TPW + x;
-    if (jv < NT) {
-#pragma unroll
-      for (int kt = 0; kt < KS_D; ++kt)
-        hfr[x][kt] = *reinterpret_cast<const frag *>(hf + (((int64_t)jv * KS_D + kt) * 64 + lane) * 8);
-#pragma unroll
-      for (int kt = 0; kt < KS_C; ++kt)
-        nfr[x][kt] = *reinterpret_cast<const frag *>(nfp + (((int64_t)jv * KS_C + kt) * 64 + lane) * 8);
-    }
-  }
-
-  {
-    const int t = tid >> 2, p = tid & 3;
-    const bool valid = t < len;
-    const int qh = h / (H / a.hq), kh = h / (H / a.hk);
-    frag qn[NV], kn[NV];
-    load_norm_row16<T, D>((const T *)a.q + ((bos + t) * a.hq + qh) * D, p, valid,
-                          a.l2norm != 0, qn);
-    load_norm_row16<T, D>((const T *)a.k + ((bos + t) * a.hk + kh) * D, p, valid,
-                          a.l2norm != 0, kn);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      *reinterpret_cast<frag *>(&sm.Qs[t][32 * i + 8 * p]) = qn[i];
-      *reinterpret_cast<frag *>(&sm.kp.Ks[t][32 * i + 8 * p]) = kn[i];
-    }
-    if (tid < 64) sm.Gs[tid] = a.Gw[ch * kChunk + tid];
-  }
-  lds_sync();
-
-  // ---- P row tile tt = wave: P^T = K Q^T leaves P rows in operand order ---
-  frag pf[KS_C];
-  {
-    const int tt = wave;
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (jt <= tt) {
-#pragma unroll
-        for (int kt = 0; kt < KS_D; ++kt) {
-          const int k0 = kt * 32 + g * 8;
-          const frag fa = *reinterpret_cast<const frag *>(&sm.kp.Ks[16 * jt + c][k0]);
-          const frag fb = *reinterpret_cast<const frag *>(&sm.Qs[16 * tt + c][k0]);
-          acc = M::mma(fa, fb, acc);
-        }
-      }
-      // acc[r] = P[t = 16tt + c][j = 16jt + 4g + r]
-      const int t = 16 * tt + c;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * jt + 4 * g + r;
-        const float pv = (j <= t) ? acc[r] * gexp(sm.Gs[t] - sm.Gs[j]) : 0.f;
-        const int s = 4 * jt + r;
-        pf[s / 8][s % 8] = (T)pv;
-      }
-    }
-  }
-  lds_sync();  // every wave is done with k
-#pragma unroll
-  for (int kt = 0; kt < KS_C; ++kt) sm.kp.Pf[wave][kt][lane] = pf[kt];
-  lds_sync();
-
-  // ---- O^T = S^T (diag(exp G) Q)^T + N^T P^T for this wave's value tiles ----
-  T *out = (T *)a.out;
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    frag qf[KS_D];
-#pragma unroll
-    for (int kt = 0; kt < KS_D; ++kt)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[kt][e] = sm.Qs[16 * tt + c][pi_idx(g, kt * 8 + e)];
-    const int t = 16 * tt + c;       // this lane's output row
-    const float gam = gexp(sm.Gs[t]);
-#pragma unroll
-    for (int x = 0; x < TPW; ++x) {
-      const int jv = wave * TPW + x;
-      if (jv >= NT) continue;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kt = 0; kt < KS_D; ++kt) acc = M::mma(hfr[x][kt], qf[kt], acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] *= gam;
-#pragma unroll
-      for (int kt = 0; kt < KS_C; ++kt)
-        if (kt * 2 <= tt)  // k-step's first token tile is not masked out
-          acc = M::mma(nfr[x][kt], sm.kp.Pf[tt][kt][lane], acc);
-      // acc[r] = O[t][16 jv + 4g + r]
-      if (t < len) {
-        typename M::half o4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o4[r] = (T)(a.scale * acc[r]);
-        *reinterpret_cast<typename M::half *>(out + ((bos + t) * H + h) * D + 16 * jv + 4 * g) = o4;
-      }
-    }
-  }
-}
-
-template <typename T, int D>
-static hipError_t launch_output_h(const Args &a, hipStream_t s) {
-  const size_t smem = sizeof(OutSmemB<T, D>);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)output_kernel_h<T, D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const int64_t blocks = a.cap * a.H;
-  if (blocks == 0) return hipSuccess;
-  output_kernel_h<T, D><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
-  return hipGetLastError();
-}
-
+// fp32 inputs (16-bit inputs form the output inside the fused state pass)
 hipError_t launch_output(const Args &a, hipStream_t s) {
-  if (a.dtype == GDN_BF16) {
-    if (a.D == 128) return launch_output_h<bf16, 128>(a, s);
-    if (a.D == 64) return launch_output_h<bf16, 64>(a, s);
-    return launch_output_h<bf16, 32>(a, s);
-  }
-  if (a.dtype == GDN_F16) {
-    if (a.D == 128) return launch_output_h<f16, 128>(a, s);
-    if (a.D == 64) return launch_output_h<f16, 64>(a, s);
-    return launch_output_h<f16, 32>(a, s);
-  }
   if (a.D == 128) return launch_output_t<float, 128>(a, s);
   if (a.D == 64) return launch_output_t<float, 64>(a, s);
   return launch_output_t<float, 32>(a, s);

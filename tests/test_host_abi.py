@@ -104,8 +104,13 @@ def test_validate_ok_and_workspace():
     p = _params(T=4096, N=2, hq=16, hk=16, hv=16)
     assert _validate(p) == 0
     need = nat.lib().gdn_prefill_workspace_size(ctypes.byref(p))
-    # 65 chunks x 16 heads x (4 blocks of 64x128 + 128x128) bf16 + G
-    assert need >= 65 * 16 * (4 * 64 * 128 * 2 + 128 * 128 * 2 + 64 * 4)
+    # 65 chunks x 16 heads x (W, Ktilde, U, q fragments: 4 blocks of 64x128,
+    # masked Q K^T: 64x64) in bf16 + G
+    assert need >= 65 * 16 * (4 * 64 * 128 * 2 + 64 * 64 * 2 + 64 * 4)
+    p32 = _params(T=4096, N=2, hq=16, hk=16, hv=16, dtype=nat.GDN_F32)
+    need32 = nat.lib().gdn_prefill_workspace_size(ctypes.byref(p32))
+    # fp32: W, Ktilde, U, N (4 blocks of 64x128) + chunk-start states 128x128
+    assert need32 >= 65 * 16 * (4 * 64 * 128 * 4 + 128 * 128 * 4 + 64 * 4)
     p.workspace_bytes = need - 1
     assert nat.lib().gdn_validate_host(ctypes.byref(p)) == code("GDN_ERR_WORKSPACE")
 
