@@ -165,8 +165,21 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
-PROF_KERNELS = {"chunk_index": "chunk_index_kernel", "intra": "intra_kernel",
-                "state": "state_kernel", "output": "output_kernel"}
+PROF_KERNELS = {"chunk_index": ("chunk_index_kernel",), "intra": ("intra_kernel", "intra_kernel_h"),
+                "state": ("state_kernel", "state_output_kernel"),
+                "output": ("output_kernel",)}
+
+
+def _phase_of(kernel_name):
+    """Phase of a kernel from its (demangled) name: the bare function name is
+    the identifier just before the template arguments or parameter list."""
+    import re
+    m = re.search(r"(\w+)\s*[<(]", kernel_name)
+    base = m.group(1) if m else kernel_name
+    for ph, names in PROF_KERNELS.items():
+        if base in names:
+            return ph
+    return None
 
 
 def _one(d, pat):
@@ -188,8 +201,8 @@ def _counters(d):
 
 def _by_phase(table):
     res = {}
-    for ph, key in PROF_KERNELS.items():
-        vals = [v for name, vs in table.items() if key in name for v in vs]
+    for ph in PROF_KERNELS:
+        vals = [v for name, vs in table.items() if _phase_of(name) == ph for v in vs]
         if vals:
             res[ph] = sum(vals) / len(vals)
     return res

@@ -236,6 +236,11 @@ int gdn_build_chunk_indices(const void *cu_seqlens, int32_t cu_type, int32_t num
 
 // The kernels' argument block for a call (workspace pointers only when a
 // workspace layout is given).
+// Above this many bytes of intermediates the fused pass finds them in HBM
+// rather than in the 256 MB last-level cache (the intra-chunk pass streams
+// q, k and v through it as well), and warming L2 ahead of the loads pays.
+constexpr int64_t kWarmBytes = 128ll << 20;
+
 static void fill_args(const gdn_prefill_params *p, const Layout *L, int num_cus, Args &a) {
   unsigned char *ws = (unsigned char *)p->workspace;
   const int64_t H = sab_heads(p), D = p->head_size;
@@ -269,6 +274,10 @@ static void fill_args(const gdn_prefill_params *p, const Layout *L, int num_cus,
       a.Qf = ws + L->Qf;
       a.Pf = ws + L->Pf;
       a.fuse = 1;
+      // W, Ktilde, U, q (64 x D each) and P (64 x 64) per chunk-head, 16-bit
+      const int64_t inter = gdn_max_chunks(p->total_tokens, p->num_seqs) * H *
+                            (4 * 64 * D + 64 * 64) * 2;
+      a.warm = inter > kWarmBytes ? 2 : 0;
     } else {
       a.Hf = ws + L->Hf;
       a.Nf = ws + L->Nf;

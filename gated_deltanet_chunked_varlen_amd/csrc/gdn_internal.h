@@ -67,6 +67,10 @@ struct Args {
   int64_t pool_rows;  // rows addressable through state_indices
   int32_t *status;
   int32_t num_cus;    // compute units of the device (launch shapes)
+  // fused 16-bit pass: chunks ahead of the current step whose operand lines
+  // one wave pulls into L2 (0: off; set when the intermediates outgrow the
+  // last-level cache and the pass would read them from HBM)
+  int32_t warm;
 };
 
 #ifdef __HIPCC__

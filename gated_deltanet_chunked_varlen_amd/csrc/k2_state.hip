@@ -340,102 +340,186 @@ __global__ void __launch_bounds__(64) state_kernel(Args a) {
 //
 // A workgroup owns one 16-column tile of one (sequence, head):
 //   wave 0      compute: the recurrence; per chunk it reads W / Ktilde / U
-//               from LDS and leaves the chunk's start-state and N fragments
-//               in an LDS buffer;
-//   OUTW waves  output: one chunk behind, O^T = S^T (diag(exp G) Q)^T +
-//               N^T P^T for the tile's 16 columns, split over token tiles,
-//               four consecutive columns per lane and 8-byte stores (only
-//               rows inside the sequence);
-//   NLW waves   loaders, in teams of TEAM waves (team j owns chunks
-//               c = j mod NLW / TEAM): per chunk they fetch W, Ktilde, the
-//               tile's U (compute part, two-slot ring) and q fragments, P
-//               fragments and the gate row (output part, three-slot ring),
-//               and store them into LDS together.
-// Step st (one LDS-only barrier each): loaders store chunk st, the compute
-// wave works on chunk st - 1, the output wave on chunk st - 2.
+//               and the gate row from an LDS slot and leaves the chunk's
+//               start-state and N fragments in an LDS buffer;
+//   waves 1, 2  output, one chunk behind: O^T = S^T (diag(exp G) Q)^T +
+//               N^T P^T for the tile's 16 columns, token tiles {0, 3} and
+//               {1, 2} (equal work: the masked P blocks are skipped); each
+//               fetches its own q and P fragments and gate values straight
+//               into registers, two chunks ahead (a three-deep ring);
+//   waves 3, 4  loaders: direct memory-to-LDS loads (no register or LDS
+//               write instructions on the way) of W, Ktilde, the tile's U
+//               and the gate row into a four-slot ring, two chunks ahead.
+// Step st (one barrier each): the loaders start chunk st + 2 and wait for
+// chunk st, the compute wave works on chunk st - 1, the output waves on
+// chunk st - 2 and start fetching chunk st.
 // ===========================================================================
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct loads into LDS: lane i's `bytes` bytes land at dst + bytes * i
+// (dst is the same for the whole wave).  Completion is counted by vmcnt.
+__device__ __forceinline__ void dma16(const void *src, unsigned char *dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *src, unsigned char *dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 4, 0, 0);
+}
+
+// One LDS slot of the fused pass: [W][Ktilde][U tile][gate row (64 floats)].
 template <typename T, int D>
-struct OutSlotGeo {
-  static constexpr int Q_BYTES = 64 * D * 2;
-  static constexpr int P_OFF = Q_BYTES;
-  static constexpr int P_BYTES = 64 * 64 * 2;
-  static constexpr int G_OFF = P_OFF + P_BYTES;
+struct DmaSlotGeo {
+  using CS = SlotGeo<T, D, 1>;
+  static constexpr int K_OFF = CS::K_OFF, U_OFF = CS::U_OFF;
+  static constexpr int G_OFF = CS::U_OFF + CS::U_TILE_BYTES;
   static constexpr int BYTES = G_OFF + 64 * 4;
-  static constexpr int NV_Q = Q_BYTES / (64 * 16);
-  static constexpr int NV_P = P_BYTES / (64 * 16);
+  static constexpr int NP = CS::NV;            // 1 KB pieces (W, Ktilde, U)
 };
 
-template <typename T, int D, int TEAM>
-struct FusedLoader {
-  using CS = SlotGeo<T, D, 1>;
-  using OS = OutSlotGeo<T, D>;
+template <typename T, int D>
+struct DmaSlotOps {
+  static constexpr bool kInterleave = true;
+  typedef typename Mfma<T>::frag frag;
+  using SG = DmaSlotGeo<T, D>;
+  static constexpr int KPL = Mfma<T>::KPL, KS_D = Geo<T, D>::KS_D, KS_C = Geo<T, D>::KS_C;
+  const unsigned char *slot;
+  int lane;
+  __device__ __forceinline__ frag w(int it, int kt) const {
+    return *reinterpret_cast<const frag *>(slot + (((it * KS_D + kt) * 64 + lane) * KPL) * sizeof(T));
+  }
+  __device__ __forceinline__ frag k(int it, int kt) const {
+    return *reinterpret_cast<const frag *>(slot + SG::K_OFF + (((it * KS_C + kt) * 64 + lane) * KPL) * sizeof(T));
+  }
+  __device__ __forceinline__ f32x4 uvec(int it) const {
+    const T *up = reinterpret_cast<const T *>(slot + SG::U_OFF) + (it * 64 + lane) * 4;
+    return f32x4{to_f32(up[0]), to_f32(up[1]), to_f32(up[2]), to_f32(up[3])};
+  }
+  __device__ __forceinline__ float glog() const {
+    return reinterpret_cast<const float *>(slot + SG::G_OFF)[kChunk - 1];
+  }
+};
+
+// Loader wave `part` of NLD: its share of a chunk's pieces (piece i goes to
+// part i % NLD; the gate row, one 4-byte-per-lane load, to the last part).
+template <typename T, int D, int NLD>
+struct DmaLoader {
+  using SG = DmaSlotGeo<T, D>;
+  static constexpr int NV_W = SG::CS::NV_W;
   static constexpr int64_t BLK = Geo<T, D>::W_ELEMS * sizeof(T) / 16;   // u32x4 per 64 x D block
-  static constexpr int64_t PBLK = 64 * 64 * sizeof(T) / 16;              // u32x4 per P block
-  static constexpr int NV = CS::NV + OS::NV_Q + OS::NV_P;                // pieces per chunk
-  static constexpr int PPW = (NV + TEAM - 1) / TEAM;
-  u32x4 v[PPW];
-  float gv;
+  static constexpr int NPC = SG::NP + 1;                                 // loads per chunk
+  static constexpr int PPW = (SG::NP + NLD - 1) / NLD;
+  // fewest loads any part issues per chunk: vmcnt thresholds built from it
+  // wait for at least the part's own older loads
+  static constexpr int MIN_PER_PART = NPC / NLD;
   int64_t uoff;
   int lane, part;
 
-  __device__ __forceinline__ void init(int jg, int ln, int pt) {
-    uoff = (int64_t)jg * (CS::U_TILE_BYTES / 16);
-    lane = ln;
-    part = pt;
-  }
-  // piece i of a chunk: W, Ktilde, U tile (compute slot), q, P (output slot)
-  __device__ __forceinline__ void issue(const Args &a, int64_t ch) {
-    const u32x4 *__restrict__ wf = reinterpret_cast<const u32x4 *>(a.Wf) + ch * BLK + lane;
-    const u32x4 *__restrict__ kf = reinterpret_cast<const u32x4 *>(a.Kf) + ch * BLK + lane;
-    const u32x4 *__restrict__ uf = reinterpret_cast<const u32x4 *>(a.Uf) + ch * BLK + uoff + lane;
-    const u32x4 *__restrict__ qf = reinterpret_cast<const u32x4 *>(a.Qf) + ch * BLK + lane;
-    const u32x4 *__restrict__ pf = reinterpret_cast<const u32x4 *>(a.Pf) + ch * PBLK + lane;
+  __device__ __forceinline__ void issue(const Args &a, int64_t ch, unsigned char *slot) const {
+    const u32x4 *wf = reinterpret_cast<const u32x4 *>(a.Wf) + ch * BLK + lane;
+    const u32x4 *kf = reinterpret_cast<const u32x4 *>(a.Kf) + ch * BLK + lane;
+    const u32x4 *uf = reinterpret_cast<const u32x4 *>(a.Uf) + ch * BLK + uoff + lane;
 #pragma unroll
     for (int m = 0; m < PPW; ++m) {
-      const int i = part + TEAM * m;
-      if (NV % TEAM == 0 || i < NV) {
+      const int i = part + NLD * m;
+      if (i < SG::NP) {
         const u32x4 *src;
-        if (i < CS::NV_W) src = wf + (int64_t)i * 64;
-        else if (i < 2 * CS::NV_W) src = kf + (int64_t)(i - CS::NV_W) * 64;
-        else if (i < CS::NV) src = uf + (int64_t)(i - 2 * CS::NV_W) * 64;
-        else if (i < CS::NV + OS::NV_Q) src = qf + (int64_t)(i - CS::NV) * 64;
-        else src = pf + (int64_t)(i - CS::NV - OS::NV_Q) * 64;
-        v[m] = *src;
+        if (i < NV_W) src = wf + (int64_t)i * 64;
+        else if (i < 2 * NV_W) src = kf + (int64_t)(i - NV_W) * 64;
+        else src = uf + (int64_t)(i - 2 * NV_W) * 64;
+        dma16(src, slot + i * 1024);
       }
     }
-    if (part == 0) gv = a.Gw[ch * kChunk + lane];
-  }
-  __device__ __forceinline__ void drop(unsigned char *cslot, unsigned char *oslot) const {
-    u32x4 *cdst = reinterpret_cast<u32x4 *>(cslot) + lane;
-    u32x4 *odst = reinterpret_cast<u32x4 *>(oslot) + lane;
-#pragma unroll
-    for (int m = 0; m < PPW; ++m) {
-      const int i = part + TEAM * m;
-      if (NV % TEAM == 0 || i < NV) {
-        if (i < CS::NV) cdst[i * 64] = v[m];
-        else odst[(i - CS::NV) * 64] = v[m];
-      }
-    }
-    if (part == 0) {
-      reinterpret_cast<float *>(oslot + OS::G_OFF)[lane] = gv;
-      if (lane == kChunk - 1) *reinterpret_cast<float *>(cslot + CS::G_OFF) = gv;
-    }
+    if (part == NLD - 1) dma4(a.Gw + ch * kChunk + lane, slot + SG::G_OFF);
   }
 };
 
-// The output of one chunk for one 16-column tile (output wave).
-template <typename T, int D, int OUTW>
-__device__ __forceinline__ void output_step(const Args &a, const unsigned char *oslot,
+// L2 warm-up of a chunk ahead of the loaders and output waves: one 4-byte
+// load per 128-byte line of everything the chunk's workgroups will read,
+// sent into a junk LDS word (nothing waits on it).  The NT workgroups of a
+// (sequence, head) share one XCD's L2 (consecutive ids map round-robin onto
+// the 8 XCDs), so each touches every NT-th line of the shared W, Ktilde, q
+// and P blocks, plus its own U tile and the gate row.
+template <typename T, int D>
+struct L2Warm {
+  static constexpr int NT = D / 16;
+  static constexpr int LINE = 128;
+  static constexpr int WL = Geo<T, D>::W_ELEMS * (int)sizeof(T) / LINE;  // lines per 64 x D block
+  static constexpr int PL = 64 * 64 * (int)sizeof(T) / LINE;             // lines per P block
+  static constexpr int SHARED = 3 * WL + PL;
+  static constexpr int UL = SlotGeo<T, D, 1>::U_TILE_BYTES / LINE;
+  static constexpr int GL = 64 * 4 / LINE;
+
+  __device__ __forceinline__ static void touch(const Args &a, int64_t ch, int jg, int lane,
+                                               unsigned char *junk) {
+    const unsigned char *wf = (const unsigned char *)a.Wf + ch * (WL * LINE);
+    const unsigned char *kf = (const unsigned char *)a.Kf + ch * (WL * LINE);
+    const unsigned char *qf = (const unsigned char *)a.Qf + ch * (WL * LINE);
+    const unsigned char *pf = (const unsigned char *)a.Pf + ch * (PL * LINE);
+#pragma unroll
+    for (int l0 = 0; l0 < SHARED; l0 += NT * 64) {
+      const int l = l0 + jg + NT * lane;
+      const int lc = min(l, SHARED - 1);
+      const unsigned char *src = lc < WL ? wf + lc * LINE
+                               : lc < 2 * WL ? kf + (lc - WL) * LINE
+                               : lc < 3 * WL ? qf + (lc - 2 * WL) * LINE
+                               : pf + (lc - 3 * WL) * LINE;
+      dma4(src, junk);
+    }
+    const unsigned char *uf = (const unsigned char *)a.Uf + ch * (WL * LINE) +
+                              (int64_t)jg * SlotGeo<T, D, 1>::U_TILE_BYTES;
+    const unsigned char *gw = (const unsigned char *)(a.Gw + ch * kChunk);
+    const int l = min(lane, UL + GL - 1);
+    dma4(l < UL ? uf + l * LINE : gw + (l - UL) * LINE, junk);
+  }
+};
+
+// vmcnt(n) for the loader's waits (n <= 63).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// One output wave's operands for one chunk: q fragments of its two token
+// tiles, the unmasked P fragments (one for the first tile, two for the
+// second) and the gate values of its two rows.
+template <typename T, int D>
+struct OutRegs {
+  typedef typename Mfma<T>::frag frag;
+  static constexpr int KS_D = Geo<T, D>::KS_D, KS_C = Geo<T, D>::KS_C;
+  static constexpr int64_t QBLK = Geo<T, D>::W_ELEMS * sizeof(T) / 16;  // u32x4 per q block
+  static constexpr int64_t PBLK = 64 * 64 * sizeof(T) / 16;            // u32x4 per P block
+  frag q[2][KS_D];
+  frag p0, p1[KS_C];
+  float g[2];
+
+  __device__ __forceinline__ void issue(const Args &a, int64_t ch, int lane, int ow) {
+    static_assert(KS_C == 2, "64-token chunks: two k-steps over a chunk");
+    const int tt0 = ow, tt1 = 3 - ow;
+    const frag *qf = reinterpret_cast<const frag *>(reinterpret_cast<const u32x4 *>(a.Qf) + ch * QBLK) + lane;
+    const frag *pf = reinterpret_cast<const frag *>(reinterpret_cast<const u32x4 *>(a.Pf) + ch * PBLK) + lane;
+#pragma unroll
+    for (int kt = 0; kt < KS_D; ++kt) {
+      q[0][kt] = qf[(tt0 * KS_D + kt) * 64];
+      q[1][kt] = qf[(tt1 * KS_D + kt) * 64];
+    }
+    p0 = pf[(tt0 * KS_C) * 64];
+#pragma unroll
+    for (int kt = 0; kt < KS_C; ++kt) p1[kt] = pf[(tt1 * KS_C + kt) * 64];
+    const int c = lane & 15;
+    g[0] = a.Gw[ch * kChunk + 16 * tt0 + c];
+    g[1] = a.Gw[ch * kChunk + 16 * tt1 + c];
+  }
+};
+
+// The output of one chunk for one 16-column tile (output wave ow).
+template <typename T, int D>
+__device__ __forceinline__ void output_regs(const Args &a, const OutRegs<T, D> &r,
                                             const typename Mfma<T>::frag *xb, int jv,
                                             int64_t tok0, int rows, int h, int lane, int ow) {
   using M = Mfma<T>;
   typedef typename M::frag frag;
-  using OS = OutSlotGeo<T, D>;
   constexpr int KS_D = Geo<T, D>::KS_D, KS_C = Geo<T, D>::KS_C;
   const int g = lane >> 4, c = lane & 15;
-  const frag *qf = reinterpret_cast<const frag *>(oslot);
-  const frag *pf = reinterpret_cast<const frag *>(oslot + OS::P_OFF);
-  const float *gs = reinterpret_cast<const float *>(oslot + OS::G_OFF);
   frag sf[KS_D], nf[KS_C];
 #pragma unroll
   for (int kt = 0; kt < KS_D; ++kt) sf[kt] = xb[kt * 64 + lane];
@@ -444,40 +528,66 @@ __device__ __forceinline__ void output_step(const Args &a, const unsigned char *
   T *out = (T *)a.out;
   const int H = a.H;
 #pragma unroll
-  for (int i = 0; i < 4 / OUTW; ++i) {
-    // token tiles of output wave ow: all four, or {0, 3} / {1, 2} (equal work)
-    const int tt = OUTW == 1 ? i : (i == 0 ? ow : 3 - ow);
+  for (int i = 0; i < 2; ++i) {
+    const int tt = i == 0 ? ow : 3 - ow;
     const int t = 16 * tt + c;  // this lane's output row
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < KS_D; ++kt) acc = M::mma(sf[kt], qf[(tt * KS_D + kt) * 64 + lane], acc);
-    const float gam = gexp(gs[t]);
+    for (int kt = 0; kt < KS_D; ++kt) acc = M::mma(sf[kt], r.q[i][kt], acc);
+    const float gam = gexp(r.g[i]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] *= gam;
+    for (int e = 0; e < 4; ++e) acc[e] *= gam;
+    // token tile 0 or 1 sees only the first k-step of P; 2 or 3 both
+    if (i == 0) {
+      acc = M::mma(nf[0], r.p0, acc);
+    } else {
 #pragma unroll
-    for (int kt = 0; kt < KS_C; ++kt)
-      if (kt * 2 <= tt)  // k-step's first token tile is not masked out
-        acc = M::mma(nf[kt], pf[(tt * KS_C + kt) * 64 + lane], acc);
-    // acc[r] = O[t][16 jv + 4g + r]
+      for (int kt = 0; kt < KS_C; ++kt) acc = M::mma(nf[kt], r.p1[kt], acc);
+    }
+    // acc[e] = O[t][16 jv + 4g + e]
     if (t < rows) {
       typename M::half o4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o4[r] = (T)(a.scale * acc[r]);
+      for (int e = 0; e < 4; ++e) o4[e] = (T)(a.scale * acc[e]);
       *reinterpret_cast<typename M::half *>(out + ((tok0 + t) * H + h) * D + 16 * jv + 4 * g) = o4;
     }
   }
 }
 
-template <typename T, int D, int OUTW, int NLW, int TEAM>
-__global__ void __launch_bounds__(64 * (1 + OUTW + NLW)) state_output_kernel(Args a) {
-  constexpr int NT = D / 16;
-  using CS = SlotGeo<T, D, 1>;
-  using OS = OutSlotGeo<T, D>;
+// One step of an output wave (st >= 2): fetch chunk st into `into` (past
+// the last chunk it repeats the last chunk), then output chunk st - 2 from
+// `proc`, fetched two steps earlier.  The step loop below runs whole rounds
+// of the three-deep ring without conditions, so the compiler's wait for
+// `proc` counts exactly the loads issued after it.
+template <typename T, int D>
+__device__ __forceinline__ void output_wave_step(const Args &a, int st, int nc, int len, int sbos,
+                                                 int64_t ch0, int jg, int h, int lane, int ow,
+                                                 OutRegs<T, D> &into, const OutRegs<T, D> &proc,
+                                                 const typename Mfma<T>::frag (*xbuf)[(Geo<T, D>::KS_D + Geo<T, D>::KS_C) * 64]) {
+  lds_sync();
+  into.issue(a, ch0 + (int64_t)min(st, nc - 1), lane, ow);
+  const int oc = st - 2;
+  output_regs<T, D>(a, proc, xbuf[oc & 1], jg, (int64_t)sbos + (int64_t)kChunk * oc,
+                    min(kChunk, len - kChunk * oc), h, lane, ow);
+}
+
+constexpr int kFusedOutWaves = 2, kFusedLoadWaves = 2, kFusedWarmWaves = 1, kFusedSlots = 4;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(64 * (1 + kFusedOutWaves + kFusedLoadWaves + kFusedWarmWaves))
+state_output_kernel(Args a) {
+  constexpr int NT = D / 16, NLD = kFusedLoadWaves, NSLOT = kFusedSlots;
+  constexpr int AHEAD = NSLOT - 2;     // chunks the loaders run ahead
+  using SG = DmaSlotGeo<T, D>;
+  using LD = DmaLoader<T, D, NLD>;
   typedef typename Mfma<T>::frag frag;
   constexpr int XB = Geo<T, D>::KS_D + Geo<T, D>::KS_C;  // fragments per chunk in xbuf
-  __shared__ __align__(16) unsigned char cslots[2][CS::BYTES];
-  __shared__ __align__(16) unsigned char oslots[3][OS::BYTES];
+  static_assert(AHEAD == 2, "the loader waits below assume two chunks ahead");
+  static_assert(AHEAD * LD::MIN_PER_PART <= 63, "vmcnt range");
+  static_assert(kFusedWarmWaves == 1, "one warm-up wave");
+  __shared__ __align__(16) unsigned char cslots[NSLOT][SG::BYTES];
   __shared__ frag xbuf[2][XB * 64];
+  __shared__ __align__(16) unsigned char junk[256];
 
   const int b = blockIdx.x;
   const int jg = (b >> 3) % NT;
@@ -508,7 +618,7 @@ __global__ void __launch_bounds__(64 * (1 + OUTW + NLW)) state_output_kernel(Arg
       lds_sync();
       if (st == 0 || st > nc) continue;
       const int cc = st - 1;
-      const LdsOps<T, D, 1> op{cslots[cc & 1], lane, 0};
+      const DmaSlotOps<T, D> op{cslots[cc % NSLOT], lane};
       chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[cc & 1]);
       if (a.ck_every > 0) {
         const int done = (cc + 1) * kChunk;
@@ -521,52 +631,69 @@ __global__ void __launch_bounds__(64 * (1 + OUTW + NLW)) state_output_kernel(Arg
     }
     if (a.out_final && a.outst && row_ok)
       write_state<T, D>(a.outst, a.out_dtype, a.out_str, row, h, vcol, g, S);
-  } else if (wave <= OUTW) {
-    // ---------------- output waves: one chunk behind the compute wave --------
-    for (int st = 0; st <= nc + 1; ++st) {
+  } else if (wave <= kFusedOutWaves) {
+    // ---------------- output waves ------------------------------------------
+    const int ow = wave - 1;
+    OutRegs<T, D> r0, r1, r2;
+    if (nc == 0) {
       lds_sync();
-      if (st < 2) continue;
-      const int oc = st - 2;
-      output_step<T, D, OUTW>(a, oslots[oc % 3], xbuf[oc & 1], jg,
-                              (int64_t)sbos + (int64_t)kChunk * oc, min(kChunk, len - kChunk * oc),
-                              h, lane, wave - 1);
+      lds_sync();
+      return;
     }
+    // steps 0 and 1 only fetch; step st >= 2 fetches chunk st and outputs
+    // chunk st - 2 (ring slot st % 3 either way)
+    lds_sync();
+    r0.issue(a, ch0, lane, ow);
+    lds_sync();
+    r1.issue(a, ch0 + (int64_t)min(1, nc - 1), lane, ow);
+    int st = 2;
+    for (; st + 3 <= nc + 2; st += 3) {
+      output_wave_step<T, D>(a, st, nc, len, sbos, ch0, jg, h, lane, ow, r2, r0, xbuf);
+      output_wave_step<T, D>(a, st + 1, nc, len, sbos, ch0, jg, h, lane, ow, r0, r1, xbuf);
+      output_wave_step<T, D>(a, st + 2, nc, len, sbos, ch0, jg, h, lane, ow, r1, r2, xbuf);
+    }
+    if (st < nc + 2) {
+      output_wave_step<T, D>(a, st, nc, len, sbos, ch0, jg, h, lane, ow, r2, r0, xbuf);
+      ++st;
+    }
+    if (st < nc + 2) output_wave_step<T, D>(a, st, nc, len, sbos, ch0, jg, h, lane, ow, r0, r1, xbuf);
+  } else if (wave == 1 + kFusedOutWaves + NLD) {
+    // ---------------- L2 warm-up wave ---------------------------------------
+    const int ahead = a.warm;
+    for (int cc = 0; cc < ahead && cc < nc; ++cc) L2Warm<T, D>::touch(a, ch0 + cc, jg, lane, junk);
+    for (int st = 0; st <= nc + 1; ++st) {
+      __builtin_amdgcn_s_barrier();
+      if (ahead > 0 && st + ahead < nc) L2Warm<T, D>::touch(a, ch0 + (int64_t)(st + ahead), jg, lane, junk);
+    }
+    wait_vm<0>();
   } else {
     // ---------------- loader waves ------------------------------------------
-    constexpr int NTEAM = NLW / TEAM;
-    static_assert(NLW % TEAM == 0, "loader waves split into whole teams");
-    const int lw = wave - 1 - OUTW, team = lw / TEAM;
-    FusedLoader<T, D, TEAM> ld;
-    ld.init(jg, lane, lw % TEAM);
-    if (team < nc) ld.issue(a, ch0 + (int64_t)team);
+    const LD ld{(int64_t)jg * (SG::CS::U_TILE_BYTES / 16), lane, wave - 1 - kFusedOutWaves};
+    for (int cc = 0; cc < AHEAD && cc < nc; ++cc) ld.issue(a, ch0 + (int64_t)cc, cslots[cc]);
     for (int st = 0; st <= nc + 1; ++st) {
-      lds_sync();
-      if (st < nc && st % NTEAM == team) {
-        ld.drop(cslots[st & 1], oslots[st % 3]);
-        if (st + NTEAM < nc) ld.issue(a, ch0 + (int64_t)(st + NTEAM));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      if (st + AHEAD < nc) ld.issue(a, ch0 + (int64_t)(st + AHEAD), cslots[(st + AHEAD) % NSLOT]);
+      // chunk st must have landed before the next barrier; the loads issued
+      // after it (chunks st + 1, st + 2 where they exist) may stay in flight
+      if (st < nc) {
+        const int newer = min(AHEAD, nc - 1 - st);
+        if (newer >= 2) wait_vm<2 * LD::MIN_PER_PART>();
+        else if (newer == 1) wait_vm<LD::MIN_PER_PART>();
+        else wait_vm<0>();
       }
     }
   }
 }
 
-#ifndef GDN_FUSED_OUTW
-#define GDN_FUSED_OUTW 2
-#endif
-#ifndef GDN_FUSED_NLW
-#define GDN_FUSED_NLW 5
-#endif
-#ifndef GDN_FUSED_TEAM
-#define GDN_FUSED_TEAM 5
-#endif
-
 template <typename T, int D>
 static hipError_t launch_state_output_t(const Args &a, hipStream_t s) {
-  constexpr int NT = D / 16, OUTW = GDN_FUSED_OUTW, NLW = GDN_FUSED_NLW, TEAM = GDN_FUSED_TEAM;
+  constexpr int NT = D / 16;
   const int64_t units = (int64_t)a.N * a.H;
   if (units == 0) return hipSuccess;
   const int64_t blocks = ((units + 7) / 8) * 8 * NT;
-  state_output_kernel<T, D, OUTW, NLW, TEAM>
-      <<<dim3((unsigned)blocks), dim3(64 * (1 + OUTW + NLW)), 0, s>>>(a);
+  state_output_kernel<T, D>
+      <<<dim3((unsigned)blocks), dim3(64 * (1 + kFusedOutWaves + kFusedLoadWaves + kFusedWarmWaves)), 0, s>>>(a);
   return hipGetLastError();
 }
 
