@@ -342,14 +342,16 @@ __global__ void __launch_bounds__(64) state_kernel(Args a) {
 //   wave 0      compute: the recurrence; per chunk it reads W / Ktilde / U
 //               and the gate row from an LDS slot and leaves the chunk's
 //               start-state and N fragments in an LDS buffer;
-//   waves 1, 2  output, one chunk behind: O^T = S^T (diag(exp G) Q)^T +
+//   waves 3, 5  output, one chunk behind: O^T = S^T (diag(exp G) Q)^T +
 //               N^T P^T for the tile's 16 columns, token tiles {0, 3} and
 //               {1, 2} (equal work: the masked P blocks are skipped); each
 //               fetches its own q and P fragments and gate values straight
 //               into registers, two chunks ahead (a three-deep ring);
-//   waves 3, 4  loaders: direct memory-to-LDS loads (no register or LDS
+//   waves 1, 2  loaders: direct memory-to-LDS loads (no register or LDS
 //               write instructions on the way) of W, Ktilde, the tile's U
-//               and the gate row into a four-slot ring, two chunks ahead.
+//               and the gate row into a four-slot ring, two chunks ahead;
+//   wave 4      L2 warm-up (when the intermediates live in HBM): touches
+//               the lines of the chunk two ahead.
 // Step st (one barrier each): the loaders start chunk st + 2 and wait for
 // chunk st, the compute wave works on chunk st - 1, the output waves on
 // chunk st - 2 and start fetching chunk st.
@@ -602,6 +604,13 @@ state_output_kernel(Args a) {
   seq_geometry(a, seq, lane, f0, nc, len, sbos);
   const int64_t ch0 = ws_index(f0, h, a.cap);
 
+  // Roles by wave index.  Waves are dealt to the CU's four SIMDs in turn
+  // (wave w on SIMD w % 4), so the compute wave (0) shares its SIMD with the
+  // light warm-up wave (4), and each loader / output wave gets a SIMD whose
+  // other wave does not issue matrix-core work on the critical path.
+  static_assert(1 + kFusedOutWaves + NLD + kFusedWarmWaves == 6, "six waves");
+  constexpr int kWarmWave = 4;
+  const bool is_out = wave == 3 || wave == 5;
   if (wave == 0) {
     // ---------------- compute wave ------------------------------------------
     const int vcol = 16 * jg + c;
@@ -631,9 +640,9 @@ state_output_kernel(Args a) {
     }
     if (a.out_final && a.outst && row_ok)
       write_state<T, D>(a.outst, a.out_dtype, a.out_str, row, h, vcol, g, S);
-  } else if (wave <= kFusedOutWaves) {
+  } else if (is_out) {
     // ---------------- output waves ------------------------------------------
-    const int ow = wave - 1;
+    const int ow = wave == 3 ? 0 : 1;
     OutRegs<T, D> r0, r1, r2;
     if (nc == 0) {
       lds_sync();
@@ -657,7 +666,7 @@ state_output_kernel(Args a) {
       ++st;
     }
     if (st < nc + 2) output_wave_step<T, D>(a, st, nc, len, sbos, ch0, jg, h, lane, ow, r0, r1, xbuf);
-  } else if (wave == 1 + kFusedOutWaves + NLD) {
+  } else if (wave == kWarmWave) {
     // ---------------- L2 warm-up wave ---------------------------------------
     const int ahead = a.warm;
     for (int cc = 0; cc < ahead && cc < nc; ++cc) L2Warm<T, D>::touch(a, ch0 + cc, jg, lane, junk);
@@ -668,7 +677,7 @@ state_output_kernel(Args a) {
     wait_vm<0>();
   } else {
     // ---------------- loader waves ------------------------------------------
-    const LD ld{(int64_t)jg * (SG::CS::U_TILE_BYTES / 16), lane, wave - 1 - kFusedOutWaves};
+    const LD ld{(int64_t)jg * (SG::CS::U_TILE_BYTES / 16), lane, wave - 1};
     for (int cc = 0; cc < AHEAD && cc < nc; ++cc) ld.issue(a, ch0 + (int64_t)cc, cslots[cc]);
     for (int st = 0; st <= nc + 1; ++st) {
       __builtin_amdgcn_s_barrier();
