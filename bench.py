@@ -174,8 +174,18 @@ def _phase_of(kernel_name):
     """Phase of a kernel from its (demangled) name: the bare function name is
     the identifier just before the template arguments or parameter list."""
     import re
-    m = re.search(r"(\w+)\s*[<(]", kernel_name)
-    base = m.group(1) if m else kernel_name
+    if kernel_name.startswith("_ZN"):          # mangled: last name of the nested name
+        pos, parts = 3, []
+        while pos < len(kernel_name) and kernel_name[pos].isdigit():
+            m = re.match(r"\d+", kernel_name[pos:])
+            n = int(m.group(0))
+            pos += len(m.group(0))
+            parts.append(kernel_name[pos:pos + n])
+            pos += n
+        base = parts[-1] if parts else kernel_name
+    else:
+        m = re.search(r"(\w+)\s*[<(]", kernel_name)
+        base = m.group(1) if m else kernel_name
     for ph, names in PROF_KERNELS.items():
         if base in names:
             return ph
