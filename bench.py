@@ -51,10 +51,11 @@ def per_token_head_bytes(wl, phase):
 
     16-bit inputs (the state pass forms the output itself):
       intra : reads q, k, v, g, beta; writes W, Ktilde, U and the q fragments
-              (64 x D each per chunk-head), the masked Q K^T (64 x 64) and the
-              64 cumulative log gates
-      state : reads W, Ktilde, U, the q fragments, Q K^T and the gates;
-              writes o
+              (64 x D each per chunk-head), the six unmasked 16 x 32 blocks of
+              the masked Q K^T (48 of 64 elements per row) and the 64
+              cumulative log gates
+      state : reads W, Ktilde, U, the q fragments, those Q K^T blocks and the
+              gates; writes o
     fp32 inputs (separate output pass):
       intra : reads k, v, g, beta; writes W, Ktilde, U and the gates
       state : reads W, Ktilde, U, G_last; writes the chunk-start state
@@ -68,9 +69,9 @@ def per_token_head_bytes(wl, phase):
     qf, kf, vf = hq / H, hk / H, hv / H
     if wl.dtype != "f32":
         if phase == "intra":
-            return (qf + kf + vf) * D * e + 8 + 4 * D * e + 64 * e + 4
+            return (qf + kf + vf) * D * e + 8 + 4 * D * e + 48 * e + 4
         if phase == "state":
-            return 4 * D * e + 64 * e + 4 + D * e
+            return 4 * D * e + 48 * e + 4 + D * e
         return 0.0
     st = D * D * e / 64.0          # chunk-start state per token
     if phase == "intra":

@@ -403,9 +403,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
         pf[sl / 8][sl % 8] = (T)pv;
       }
     }
+    // the blocks with 2 kt > tt are all zero; the fused pass does not read them
 #pragma unroll
     for (int kt = 0; kt < KS_C; ++kt)
-      *reinterpret_cast<frag *>(pf_out + (((int64_t)tt * KS_C + kt) * 64 + lane) * 8) = pf[kt];
+      if (2 * kt <= tt)
+        *reinterpret_cast<frag *>(pf_out + (((int64_t)tt * KS_C + kt) * 64 + lane) * 8) = pf[kt];
 #pragma unroll
     for (int kt = 0; kt < KS_D; ++kt) {
       frag qf;
