@@ -16,6 +16,7 @@ stream, in K further steps) and the CPU oracle's throughput on the same
 workload (a bounded number of repetitions on this host's cores).
 
     python bench.py [--steps K] [--warmup W] [--workload c2]
+    python bench.py --workload decode       # the decode step, its own line
     python bench.py --copy-calibration      # plain 1 GiB copies, for counters
     python bench.py --summarize <workload> <rocprofv3 output dirs...> <command>
 """
@@ -41,7 +42,7 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 matrix peak
 PHASES = ["chunk_index", "intra", "state", "output"]
 KERNEL_SOURCES = {
     "chunk_index": "k0_chunk_index.hip", "intra": "k1_intra.hip",
-    "state": "k2_state.hip", "output": "k3_output.hip",
+    "state": "k2_state.hip", "output": "k3_output.hip", "decode": "k4_decode.hip",
 }
 
 
@@ -84,6 +85,17 @@ def per_token_head_bytes(wl, phase):
 
 
 FLOPS_PER_TOKEN_HEAD = lambda D: 2 * (5 * 64 * D + 3 * D * D)   # eight chunk GEMMs
+
+
+def decode_bytes_per_seq_head(wl):
+    """Algorithmic HBM bytes of one decode step per (sequence, sab head):
+    the D x D state read and written in its pool dtype, q, k, v (shared
+    heads counted once per source head), g and beta read, o written."""
+    D, H = wl.D, wl.H
+    e = 4 if wl.dtype == "f32" else 2
+    se = {"f32": 4, "bf16": 2, "f16": 2}[wl.initial_state_dtype]
+    hq, hk, hv = wl.q.shape[1], wl.k.shape[1], wl.v.shape[1]
+    return 2 * D * D * se + (hq + hk + hv) / H * D * e + 8 + D * e
 
 
 def hip():
@@ -168,7 +180,7 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 
 PROF_KERNELS = {"chunk_index": ("chunk_index_kernel",), "intra": ("intra_kernel", "intra_kernel_h"),
                 "state": ("state_kernel", "state_output_kernel"),
-                "output": ("output_kernel",)}
+                "output": ("output_kernel",), "decode": ("decode_kernel",)}
 
 
 def _phase_of(kernel_name):
@@ -269,6 +281,88 @@ def summarize(argv):
     print(out)
 
 
+def bench_decode(args):
+    """The decode step on the decode workload: one JSON line of its own."""
+    import torch
+    from gated_deltanet_chunked_varlen_amd import workloads as W
+    from gated_deltanet_chunked_varlen_amd import api
+    from gated_deltanet_chunked_varlen_amd import _native as nat
+    from tests import gdn_testlib as tl
+
+    wl = W.WORKLOADS["decode"]()
+    d = tl.to_device(wl)
+    N, H, D = wl.N, wl.H, wl.D
+    pool = d["initial_state"]
+    p, out, outst = api.make_params(
+        d["q"], d["k"], d["v"], g=d["g"], beta=d["beta"], scale=wl.scale,
+        initial_state=pool, output_final_state=True,
+        use_qk_l2norm_in_kernel=wl.l2norm_in_kernel, output_state=pool,
+        state_indices=d["state_indices"], decode=True)
+    lib = nat.lib()
+    L = hip()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call():
+        rc = lib.gdn_decode(ctypes.byref(p), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(nat.status_string(rc))
+
+    for _ in range(max(args.warmup, 1)):
+        call()
+    K = args.steps
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(K):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    # the decode step is one kernel: HIP events on the call's stream around it
+    pairs = [(new_event(L), new_event(L)) for _ in range(K)]
+    rec = L.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    for a_, b_ in pairs:
+        if rec(a_, ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+        call()
+        if rec(b_, ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+    torch.cuda.synchronize()
+    dom_ms = sum(elapsed_ms(L, a_, b_) for a_, b_ in pairs) / K
+    for a_, b_ in pairs:
+        L.hipEventDestroy(a_)
+        L.hipEventDestroy(b_)
+    bytes_launch = decode_bytes_per_seq_head(wl) * N * H
+    achieved = bytes_launch / (dom_ms / 1e3) / 1e9
+    res = {
+        "metric": "GDN decode tokens/s (one new token per sequence per step), H=16 D=128",
+        "value": N * K / (ms_total / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_total / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded numpy draws, see workloads.py)",
+        "config": {"workload": wl.name, "num_seqs": N, "tokens_per_seq": 1,
+                   "num_heads": H, "head_size": D, "state_pool_rows": int(pool.shape[0]),
+                   "state_dtype": wl.initial_state_dtype, "qk_l2norm_in_kernel": wl.l2norm_in_kernel,
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "decode", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": load_traffic("decode", wl.name), "avg_launch_ms": dom_ms,
+                     "timing": "HIP events around the call in each of K further steps",
+                     "algorithmic_bytes_per_launch": bytes_launch},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
         summarize(sys.argv[2:])
@@ -279,7 +373,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2",
-                    help="c2 (default, the headline); c1..c5 for analysis")
+                    help="c2 (default, the headline); c1..c5 for analysis; "
+                         "decode for the decode step (its own JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -300,6 +395,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workload == "decode":
+        bench_decode(args)
         return
 
     from gated_deltanet_chunked_varlen_amd import workloads as W

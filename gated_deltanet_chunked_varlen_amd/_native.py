@@ -18,7 +18,7 @@ ERRORS = {
     -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_HEAD_RATIO",
     -4: "GDN_ERR_DTYPE", -5: "GDN_ERR_CHECKPOINT", -6: "GDN_ERR_STATE",
     -7: "GDN_ERR_MAX_SEQLEN", -8: "GDN_ERR_WORKSPACE", -9: "GDN_ERR_STRIDES",
-    -10: "GDN_ERR_DEVICE", -11: "GDN_ERR_LAUNCH",
+    -10: "GDN_ERR_DEVICE", -11: "GDN_ERR_LAUNCH", -12: "GDN_ERR_ALIGN",
 }
 ERR_CODE = {v: k for k, v in ERRORS.items()}
 STATUS_CU_SEQLENS = 1

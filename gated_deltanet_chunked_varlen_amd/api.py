@@ -30,7 +30,8 @@ _INDEX_TYPES = {torch.int32: nat.GDN_I32, torch.int64: nat.GDN_I64}
 
 _VALUE_ERRORS = {"GDN_ERR_NULL", "GDN_ERR_SHAPE", "GDN_ERR_HEAD_RATIO",
                  "GDN_ERR_DTYPE", "GDN_ERR_CHECKPOINT", "GDN_ERR_STATE",
-                 "GDN_ERR_MAX_SEQLEN", "GDN_ERR_WORKSPACE", "GDN_ERR_STRIDES"}
+                 "GDN_ERR_MAX_SEQLEN", "GDN_ERR_WORKSPACE", "GDN_ERR_STRIDES",
+                 "GDN_ERR_ALIGN"}
 
 
 def _raise(rc: int):

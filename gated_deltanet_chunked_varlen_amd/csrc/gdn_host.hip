@@ -96,6 +96,14 @@ void fill_strides(const int64_t in[4], int64_t H, int64_t D, int64_t out[4]) {
   }
 }
 
+// q, k, v and output move in 16-byte vector accesses.
+bool io_aligned(const gdn_prefill_params *p) {
+  const void *ptrs[4] = {p->q, p->k, p->v, p->output};
+  for (const void *x : ptrs)
+    if ((uintptr_t)x % 16 != 0) return false;
+  return true;
+}
+
 // Checks that the current device is a gfx950 and reports its CU count
 // (cached per device).
 int check_device(int *num_cus = nullptr) {
@@ -141,6 +149,7 @@ const char *gdn_status_string(int code) {
     case GDN_ERR_STRIDES: return "state strides must be all zero (contiguous) or positive and non-overlapping";
     case GDN_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
     case GDN_ERR_LAUNCH: return "kernel launch failed";
+    case GDN_ERR_ALIGN: return "q, k, v and output must be 16-byte aligned and the workspace 256-byte aligned";
     case (int)GDN_STATUS_CU_SEQLENS: return "status: cu_seqlens not non-decreasing within [0, total_tokens]";
     case (int)GDN_STATUS_CHECKPOINT_STARTS: return "status: checkpoint_cu_starts differs from the prefix sum of floor(len / n)";
     case (int)GDN_STATUS_STATE_INDEX: return "status: a state index is outside [0, pool_size)";
@@ -180,6 +189,7 @@ int gdn_validate_host(const gdn_prefill_params *p) {
   if (rc != GDN_OK) return rc;
   const int64_t T = p->total_tokens, N = p->num_seqs, H = sab_heads(p), D = p->head_size;
   if (T > 0 && (!p->q || !p->k || !p->v || !p->output)) return GDN_ERR_NULL;
+  if (!io_aligned(p)) return GDN_ERR_ALIGN;
   if (p->cu_seqlens && !valid_itype(p->cu_seqlens_type)) return GDN_ERR_DTYPE;
   // states
   if (p->initial_state && !valid_state_dtype(p->initial_state_dtype)) return GDN_ERR_DTYPE;
@@ -214,6 +224,7 @@ int gdn_validate_host(const gdn_prefill_params *p) {
   // workspace
   const size_t need = plan(p).total;
   if (p->workspace_bytes < need || (need > 0 && !p->workspace)) return GDN_ERR_WORKSPACE;
+  if ((uintptr_t)p->workspace % kAlign != 0) return GDN_ERR_ALIGN;
   return GDN_OK;
 }
 
@@ -369,6 +380,7 @@ int gdn_validate_decode_host(const gdn_prefill_params *p) {
     return GDN_ERR_CHECKPOINT;
   const int64_t N = p->num_seqs, H = sab_heads(p), D = p->head_size;
   if (N > 0 && (!p->q || !p->k || !p->v || !p->output)) return GDN_ERR_NULL;
+  if (!io_aligned(p)) return GDN_ERR_ALIGN;
   if (p->initial_state && !valid_state_dtype(p->initial_state_dtype)) return GDN_ERR_DTYPE;
   if (p->output_final_state) {
     if (!p->output_state) return GDN_ERR_STATE;

@@ -23,42 +23,66 @@
 
 namespace gdn {
 
+// A lane's E consecutive elements of one state column (row v of the [V, K]
+// layout).  With unit element stride and 16-byte alignment of every row
+// segment (checked per call) they move as whole 16-byte (or E-element)
+// vector accesses; otherwise element by element.
 template <typename St, int E>
-__device__ __forceinline__ void load_col(const St *p, int64_t str3, float (&s)[E]) {
-  if (str3 == 1) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) s[e] = to_f32(p[e]);
-  } else {
-#pragma unroll
-    for (int e = 0; e < E; ++e) s[e] = to_f32(p[(int64_t)e * str3]);
-  }
-}
+struct ColIO {
+  static constexpr int BYTES = E * (int)sizeof(St);
+  static constexpr int ALIGN = BYTES < 16 ? BYTES : 16;
 
-template <typename St, int E>
-__device__ __forceinline__ void store_col(St *p, int64_t str3, const float (&s)[E]) {
-  if (str3 == 1) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) p[e] = from_f32<St>(s[e]);
-  } else {
-#pragma unroll
-    for (int e = 0; e < E; ++e) p[(int64_t)e * str3] = from_f32<St>(s[e]);
+  __device__ __forceinline__ static bool vec_ok(const void *base, const int64_t *str) {
+    return str[3] == 1 && ((uintptr_t)base % ALIGN) == 0 &&
+           (str[0] * (int64_t)sizeof(St)) % ALIGN == 0 &&
+           (str[1] * (int64_t)sizeof(St)) % ALIGN == 0 &&
+           (str[2] * (int64_t)sizeof(St)) % ALIGN == 0;
   }
+  __device__ __forceinline__ static void load(const St *p, int64_t str3, bool vec, float (&s)[E]) {
+    if (vec) {
+      St t[E];
+      __builtin_memcpy(t, __builtin_assume_aligned(p, ALIGN), BYTES);
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] = to_f32(t[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] = to_f32(p[(int64_t)e * str3]);
+    }
+  }
+  __device__ __forceinline__ static void store(St *p, int64_t str3, bool vec, const float (&s)[E]) {
+    if (vec) {
+      St t[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) t[e] = from_f32<St>(s[e]);
+      __builtin_memcpy(__builtin_assume_aligned(p, ALIGN), t, BYTES);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) p[(int64_t)e * str3] = from_f32<St>(s[e]);
+    }
+  }
+};
+
+template <int E>
+__device__ __forceinline__ bool state_vec_ok(const void *base, int dtype, const int64_t *str) {
+  if (dtype == GDN_F32) return ColIO<float, E>::vec_ok(base, str);
+  if (dtype == GDN_BF16) return ColIO<bf16, E>::vec_ok(base, str);
+  return ColIO<_Float16, E>::vec_ok(base, str);
 }
 
 template <int E>
 __device__ __forceinline__ void load_state_col(const void *base, int dtype, const int64_t *str,
-                                               int64_t off, float (&s)[E]) {
-  if (dtype == GDN_F32) load_col<float, E>((const float *)base + off, str[3], s);
-  else if (dtype == GDN_BF16) load_col<bf16, E>((const bf16 *)base + off, str[3], s);
-  else load_col<_Float16, E>((const _Float16 *)base + off, str[3], s);
+                                               int64_t off, bool vec, float (&s)[E]) {
+  if (dtype == GDN_F32) ColIO<float, E>::load((const float *)base + off, str[3], vec, s);
+  else if (dtype == GDN_BF16) ColIO<bf16, E>::load((const bf16 *)base + off, str[3], vec, s);
+  else ColIO<_Float16, E>::load((const _Float16 *)base + off, str[3], vec, s);
 }
 
 template <int E>
 __device__ __forceinline__ void store_state_col(void *base, int dtype, const int64_t *str,
-                                                int64_t off, const float (&s)[E]) {
-  if (dtype == GDN_F32) store_col<float, E>((float *)base + off, str[3], s);
-  else if (dtype == GDN_BF16) store_col<bf16, E>((bf16 *)base + off, str[3], s);
-  else store_col<_Float16, E>((_Float16 *)base + off, str[3], s);
+                                                int64_t off, bool vec, const float (&s)[E]) {
+  if (dtype == GDN_F32) ColIO<float, E>::store((float *)base + off, str[3], vec, s);
+  else if (dtype == GDN_BF16) ColIO<bf16, E>::store((bf16 *)base + off, str[3], vec, s);
+  else ColIO<_Float16, E>::store((_Float16 *)base + off, str[3], vec, s);
 }
 
 // Sum over the 16 lanes of a column group.
@@ -110,13 +134,12 @@ __global__ void __launch_bounds__(256) decode_kernel(Args a) {
   const int qh = h / (H / a.hq), kh = h / (H / a.hk), vh = h / (H / a.hv);
   float q[E], k[E];
   {
+    // rows are contiguous and D-element aligned, so a lane's E elements are
+    // one aligned vector access
     const T *qp = (const T *)a.q + ((int64_t)seq * a.hq + qh) * D + l16 * E;
     const T *kp = (const T *)a.k + ((int64_t)seq * a.hk + kh) * D + l16 * E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      q[e] = to_f32(qp[e]);
-      k[e] = to_f32(kp[e]);
-    }
+    ColIO<T, E>::load(qp, 1, true, q);
+    ColIO<T, E>::load(kp, 1, true, k);
     if (a.l2norm) {
       // x / sqrt(sum x^2 + eps) in fp32, rounded back to the input type as
       // the prefill kernels do
@@ -141,37 +164,50 @@ __global__ void __launch_bounds__(256) decode_kernel(Args a) {
   const T *vp = (const T *)a.v + ((int64_t)seq * a.hv + vh) * D;
   T *op = (T *)a.out + ((int64_t)seq * H + h) * D;
 
+  // all four columns' state loads first, so a wave has 4 x D / 16 elements
+  // per lane in flight; then the updates; then the stores
+  const bool vin = a.init && ok && state_vec_ok<E>(a.init, a.init_dtype, a.init_str);
+  const bool vout = a.outst && state_vec_ok<E>(a.outst, a.out_dtype, a.out_str);
+  float s[4][E], vv[4];
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int v = grp * 16 + pass * 4 + cq;
-    float s[E];
     if (a.init && ok) {
       load_state_col<E>(a.init, a.init_dtype, a.init_str,
                         row * a.init_str[0] + (int64_t)h * a.init_str[1] +
                             (int64_t)v * a.init_str[2] + (int64_t)(l16 * E) * a.init_str[3],
-                        s);
+                        vin, s[pass]);
     } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) s[e] = 0.f;
+      for (int e = 0; e < E; ++e) s[pass][e] = 0.f;
     }
+    vv[pass] = to_f32(vp[v]);
+  }
+  float o[4];
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
     float d1 = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) d1 = fmaf(k[e], s[e], d1);
+    for (int e = 0; e < E; ++e) d1 = fmaf(k[e], s[pass][e], d1);
     d1 = sum16(d1);
-    const float coef = beta * (to_f32(vp[v]) - alpha * d1);
-    float o = 0.f;
+    const float coef = beta * (vv[pass] - alpha * d1);
+    float ov = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      s[e] = fmaf(alpha, s[e], coef * k[e]);
-      o = fmaf(q[e], s[e], o);
+      s[pass][e] = fmaf(alpha, s[pass][e], coef * k[e]);
+      ov = fmaf(q[e], s[pass][e], ov);
     }
-    o = sum16(o);
+    o[pass] = sum16(ov);
+  }
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int v = grp * 16 + pass * 4 + cq;
     if (ok && a.out_final && a.outst)
       store_state_col<E>(a.outst, a.out_dtype, a.out_str,
                          row * a.out_str[0] + (int64_t)h * a.out_str[1] +
                              (int64_t)v * a.out_str[2] + (int64_t)(l16 * E) * a.out_str[3],
-                         s);
-    if (l16 == 0) op[v] = from_f32<T>(a.scale * o);
+                         vout, s[pass]);
+    if (l16 == 0) op[v] = from_f32<T>(a.scale * o[pass]);
   }
 }
 

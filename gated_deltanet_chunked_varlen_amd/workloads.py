@@ -261,10 +261,21 @@ def c5_long_single() -> Workload:
                 name="long_L262144_h32_d128_bf16")
 
 
+def decode_batch() -> Workload:
+    """One decode step for 256 sequences (one new token each), 16 heads, head
+    size 128, bf16, in-kernel q/k L2 norm, alpha ~ U[0.9, 1], fp32 512-slot
+    state pool ~ N(0, 0.02) read and written in place through unique
+    state_indices (the serving shape of the prefill's pool)."""
+    return make(1005, [1] * 256, 16, 16, 16, 128, "bf16",
+                l2norm_in_kernel=True, init="pool", pool_size=512,
+                in_place_pool=True, name="decode_b256_h16_d128_bf16_pool512")
+
+
 WORKLOADS = {
     "c1": c1_single_small,
     "c2": c2_two_by_2048,
     "c3": c3_ragged_pool,
     "c4": c4_gva_checkpoints,
     "c5": c5_long_single,
+    "decode": decode_batch,
 }

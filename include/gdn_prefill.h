@@ -57,6 +57,9 @@ typedef enum { GDN_I32 = 0, GDN_I64 = 1 } gdn_itype;
 #define GDN_ERR_STRIDES -9       /* state strides not positive/non-overlapping */
 #define GDN_ERR_DEVICE -10       /* current device is not gfx950 */
 #define GDN_ERR_LAUNCH -11       /* a kernel launch failed */
+#define GDN_ERR_ALIGN -12        /* q, k, v or output not 16-byte aligned, or the
+                                    workspace not 256-byte aligned (the kernels
+                                    move them in 16-byte vector accesses) */
 
 /* Device status bits (written to *status by every call). */
 #define GDN_STATUS_CU_SEQLENS 1u        /* cu_seqlens not non-decreasing within [0, T] */
@@ -94,6 +97,9 @@ typedef enum { GDN_I32 = 0, GDN_I64 = 1 } gdn_itype;
  *   state after j*n of its tokens, at row checkpoint_cu_starts[i] + j - 1.
  *   max_seqlen: 0 = unknown; otherwise must satisfy ceil(T/N) <= max_seqlen
  *   <= T (gitcode section "约束与注意点").
+ *   Alignment: q, k, v and output start on 16-byte boundaries and the
+ *   workspace on a 256-byte boundary (GDN_ERR_ALIGN otherwise; torch
+ *   allocations satisfy both).
  */
 typedef struct gdn_prefill_params {
   int64_t total_tokens;   /* T >= 0 */
@@ -177,7 +183,10 @@ int gdn_prefill_timed(const gdn_prefill_params *p, void *stream,
  *     cu_seqlens must be NULL (GDN_ERR_SHAPE otherwise); q/k/v are
  *     [N, heads, D], g and beta [N, H], output [N, H, D];
  *   - checkpoint_every_n_tokens must be 0 and the checkpoint buffers NULL
- *     (GDN_ERR_CHECKPOINT); max_seqlen and the workspace are ignored.
+ *     (GDN_ERR_CHECKPOINT); max_seqlen and the workspace are ignored;
+ *   - q, k, v and output 16-byte aligned as in gdn_prefill (GDN_ERR_ALIGN);
+ *     states whose rows are not 16-byte aligned are read and written element
+ *     by element.
  * States, pools (output_state may alias initial_state), head sharing,
  * defaults, l2 normalisation and the status word behave as in gdn_prefill;
  * only GDN_STATUS_STATE_INDEX can be set.  Duplicate state_indices race.

@@ -113,6 +113,10 @@ def test_validate_ok_and_workspace():
     assert need32 >= 65 * 16 * (4 * 64 * 128 * 4 + 128 * 128 * 4 + 64 * 4)
     p.workspace_bytes = need - 1
     assert nat.lib().gdn_validate_host(ctypes.byref(p)) == code("GDN_ERR_WORKSPACE")
+    # the workspace must start on a 256-byte boundary
+    p.workspace_bytes = need
+    p.workspace = ctypes.c_void_p(0x2010)
+    assert nat.lib().gdn_validate_host(ctypes.byref(p)) == code("GDN_ERR_ALIGN")
 
 
 @pytest.mark.parametrize("kw,err", [
@@ -123,6 +127,8 @@ def test_validate_ok_and_workspace():
     (dict(hq=4, hk=4, hv=6), "GDN_ERR_HEAD_RATIO"),
     (dict(dtype=7), "GDN_ERR_DTYPE"),
     (dict(extra=dict(q=None)), "GDN_ERR_NULL"),
+    (dict(extra=dict(q=ctypes.c_void_p(0x1008))), "GDN_ERR_ALIGN"),
+    (dict(extra=dict(output=ctypes.c_void_p(0x1004))), "GDN_ERR_ALIGN"),
     (dict(extra=dict(checkpoint_every_n_tokens=100,
                      state_checkpoints=ctypes.c_void_p(8),
                      checkpoint_cu_starts=ctypes.c_void_p(8))), "GDN_ERR_CHECKPOINT"),
@@ -190,6 +196,7 @@ def test_validate_decode_ok():
     (dict(T=8, N=8, cu=False, extra=dict(checkpoint_every_n_tokens=64)), "GDN_ERR_CHECKPOINT"),
     (dict(T=8, N=8, cu=False, extra=dict(output_final_state=1)), "GDN_ERR_STATE"),
     (dict(T=8, N=8, cu=False, extra=dict(k=None)), "GDN_ERR_NULL"),
+    (dict(T=8, N=8, cu=False, extra=dict(v=ctypes.c_void_p(0x1002))), "GDN_ERR_ALIGN"),
 ])
 def test_validate_decode_errors(kw, err):
     assert _validate_decode(_params(**kw)) == code(err)
