@@ -129,9 +129,10 @@ def expected_pool(wl, orc_final):
     return pool
 
 
-def run_gpu_decode(wl, device="cuda", status=False):
+def run_gpu_decode(wl, device="cuda", status=False, **over):
     """One decode step on the HIP path for a workload whose sequences all have
-    length 1 (token i = sequence i); same return dict as run_gpu."""
+    length 1 (token i = sequence i); same return dict as run_gpu.  Keyword
+    overrides replace the call's arguments (e.g. strided state views)."""
     torch = _torch()
     from gated_deltanet_chunked_varlen_amd import gated_delta_rule_decode
     assert all(int(x) == 1 for x in np.diff(wl.cu_seqlens))
@@ -155,6 +156,7 @@ def run_gpu_decode(wl, device="cuda", status=False):
     st = torch.full((1,), -1, dtype=torch.int32, device=device) if status else None
     if st is not None:
         kw["status"] = st
+    kw.update(over)
     res = gated_delta_rule_decode(d["q"], d["k"], d["v"], **kw)
     out, fin = (res if wl.output_final_state else (res, None))
     torch.cuda.synchronize()

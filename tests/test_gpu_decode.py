@@ -62,6 +62,21 @@ def test_decode_head_sharing(hq, hk, hv):
     _check(wl, tl.run_gpu_decode(wl), tl.run_oracle(wl))
 
 
+def test_decode_strided_states():
+    """State views: the initial state with a non-contiguous head/row order but
+    unit element stride (16-byte vector path), the final state with a
+    non-unit element stride (element-by-element path)."""
+    wl = _dec(46, 24, init="seq")
+    H, D, N = wl.H, wl.D, wl.N
+    base = torch.from_numpy(np.ascontiguousarray(
+        wl.initial_state.transpose(1, 0, 2, 3))).cuda()       # [H, N, V, K]
+    init = base.permute(1, 0, 2, 3)                            # [N, H, V, K] view
+    outbuf = torch.zeros((H, D, D, N), dtype=torch.float32, device="cuda")
+    outst = outbuf.permute(3, 0, 1, 2)                         # [N, H, V, K] view
+    gpu = tl.run_gpu_decode(wl, initial_state=init, output_state=outst)
+    _check(wl, dict(gpu, final=outst.cpu().numpy().astype(np.float64)), tl.run_oracle(wl))
+
+
 def test_decode_no_gates_no_state_bf16_final():
     wl = _dec(44, 9, gates=False, init=None, final_state_dtype="bf16")
     _check(wl, tl.run_gpu_decode(wl), tl.run_oracle(wl))
