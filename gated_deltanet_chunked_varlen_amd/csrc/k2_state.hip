@@ -208,10 +208,37 @@ __device__ __forceinline__ void chunk_step(const Args &a, const Ops &op,
   }
 }
 
+// A lane holds S[16 it + 4 g + r][vcol], r = 0..3: four consecutive k of
+// row vcol of the stored [V, K] state.  With unit k stride and every such
+// run aligned to its size (checked per call), each run moves as one vector
+// access (16 bytes in fp32, 8 in 16 bits); otherwise element by element.
+template <typename St>
+__device__ __forceinline__ bool state_runs_aligned(const void *p, const int64_t str[4]) {
+  constexpr int A = 4 * (int)sizeof(St);
+  return str[3] == 1 && (uintptr_t)p % A == 0 && (str[0] * (int64_t)sizeof(St)) % A == 0 &&
+         (str[1] * (int64_t)sizeof(St)) % A == 0 && (str[2] * (int64_t)sizeof(St)) % A == 0;
+}
+
+template <typename St>
+struct Run4 {
+  typedef St v4 __attribute__((ext_vector_type(4)));
+};
+
 template <typename St, int D>
 __device__ __forceinline__ void write_state_t(St *p, const int64_t str[4], int64_t row, int h,
                                               int vcol, int g, const float (&S)[D / 16][4]) {
   const int64_t base = row * str[0] + (int64_t)h * str[1] + (int64_t)vcol * str[2];
+  if (state_runs_aligned<St>(p, str)) {
+    typedef typename Run4<St>::v4 v4;
+#pragma unroll
+    for (int it = 0; it < D / 16; ++it) {
+      v4 x;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = from_f32<St>(S[it][r]);
+      *reinterpret_cast<v4 *>(p + base + 16 * it + 4 * g) = x;
+    }
+    return;
+  }
 #pragma unroll
   for (int it = 0; it < D / 16; ++it)
 #pragma unroll
@@ -231,6 +258,16 @@ template <typename St, int D>
 __device__ __forceinline__ void read_state_t(const St *p, const int64_t str[4], int64_t row, int h,
                                              int vcol, int g, float (&S)[D / 16][4]) {
   const int64_t base = row * str[0] + (int64_t)h * str[1] + (int64_t)vcol * str[2];
+  if (state_runs_aligned<St>(p, str)) {
+    typedef typename Run4<St>::v4 v4;
+#pragma unroll
+    for (int it = 0; it < D / 16; ++it) {
+      const v4 x = *reinterpret_cast<const v4 *>(p + base + 16 * it + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[it][r] = to_f32(x[r]);
+    }
+    return;
+  }
 #pragma unroll
   for (int it = 0; it < D / 16; ++it)
 #pragma unroll
