@@ -318,10 +318,13 @@ def bench_decode(args):
     stop.record()
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(stop)
-    # the decode step is one kernel: HIP events on the call's stream around it
+    # the decode step is one kernel: HIP events on the call's stream around
+    # it, after untimed calls so that the clock has settled again
     pairs = [(new_event(L), new_event(L)) for _ in range(K)]
     rec = L.hipEventRecord
     rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    for _ in range(min(max(args.warmup, 1), 200)):
+        call()
     for a_, b_ in pairs:
         if rec(a_, ctypes.c_void_p(stream)) != 0:
             raise RuntimeError("hipEventRecord failed")
@@ -371,7 +374,7 @@ def main():
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="c2",
                     help="c2 (default, the headline); c1..c5 for analysis; "
                          "decode for the decode step (its own JSON line)")
@@ -435,17 +438,16 @@ def main():
         if rc != 0:
             raise RuntimeError(nat.status_string(rc))
 
-    # warm-up, with every phase timed to find the dominant kernel
-    ev = [[new_event(L) for _ in range(5)] for _ in range(max(args.warmup, 1))]
-    for i in range(max(args.warmup, 1)):
-        call((ctypes.c_void_p * 5)(*ev[i]))
-    torch.cuda.synchronize()
-    # median over the warm-up calls after the first (which pays one-time set-up)
-    used = ev[1:] if len(ev) > 1 else ev
-    phase_ms = {ph: float(np.median([elapsed_ms(L, e[j], e[j + 1]) for e in used]))
-                for j, ph in enumerate(PHASES)}
-    dom = max(PHASES, key=lambda ph: phase_ms[ph])
-    di = PHASES.index(dom)
+    # warm-up: W calls, the last ones with every phase timed (to find the
+    # dominant kernel afterwards).  The timed region follows at once: after a
+    # few ms of idleness the GPU clock drops and needs ~10 ms of work to come
+    # back, so nothing (no event reads) may sit between the two.
+    W_ = max(args.warmup, 1)
+    n_ev = min(W_, 50)
+    ev = [[new_event(L) for _ in range(5)] for _ in range(n_ev)]
+    for i in range(W_):
+        j = i - (W_ - n_ev)
+        call((ctypes.c_void_p * 5)(*ev[j]) if j >= 0 else none5)
 
     # timed region: exactly K steps, each the call as a user makes it
     K = args.steps
@@ -459,15 +461,30 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(stop)
+
+    # median over the timed warm-up calls (after the very first call, which
+    # pays one-time set-up)
+    used = ev[1:] if (len(ev) > 1 and n_ev == W_) else ev
+    phase_ms = {ph: float(np.median([elapsed_ms(L, e[j], e[j + 1]) for e in used]))
+                for j, ph in enumerate(PHASES)}
+    dom = max(PHASES, key=lambda ph: phase_ms[ph])
+    di = PHASES.index(dom)
+
     # roofline region: K more steps with HIP events recorded on the call's own
     # stream around the dominant kernel of every step.  The two extra events
     # per step lengthen each step a little, so they stay out of the region
     # that gives the throughput.
+    # It is preceded by untimed calls, so that it too runs on a settled clock.
     pairs = [(new_event(L), new_event(L)) for _ in range(K)]
+    e5s = []
     for i in range(K):
         e5 = (ctypes.c_void_p * 5)()
         e5[di], e5[di + 1] = pairs[i][0], pairs[i][1]
-        call(e5)
+        e5s.append(e5)
+    for i in range(min(W_, 200)):
+        call()
+    for i in range(K):
+        call(e5s[i])
     torch.cuda.synchronize()
     dom_ms = sum(elapsed_ms(L, a, b) for a, b in pairs) / K
     for row in ev:
