@@ -10,7 +10,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgdn_prefill.so")
 
-GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
+GDN_F32, GDN_BF16, GDN_F16, GDN_FP8_E4M3, GDN_FP8_E5M2 = 0, 1, 2, 3, 4
 GDN_I32, GDN_I64 = 0, 1
 
 GDN_OK = 0

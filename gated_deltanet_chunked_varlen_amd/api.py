@@ -25,7 +25,8 @@ from . import _native as nat
 _QKV_DTYPES = {torch.float32: nat.GDN_F32, torch.bfloat16: nat.GDN_BF16,
                torch.float16: nat.GDN_F16}
 _STATE_DTYPES = {torch.float32: nat.GDN_F32, torch.bfloat16: nat.GDN_BF16,
-                 torch.float16: nat.GDN_F16}
+                 torch.float16: nat.GDN_F16, torch.float8_e4m3fn: nat.GDN_FP8_E4M3,
+                 torch.float8_e5m2: nat.GDN_FP8_E5M2}
 _INDEX_TYPES = {torch.int32: nat.GDN_I32, torch.int64: nat.GDN_I64}
 
 _VALUE_ERRORS = {"GDN_ERR_NULL", "GDN_ERR_SHAPE", "GDN_ERR_HEAD_RATIO",

@@ -52,6 +52,69 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
 
+// ---------------------------------------------------------------------------
+// 8-bit float storage of states (OCP FP8: E4M3 with no infinities, max 448;
+// E5M2, max 57344).  Only states are stored this way: a store rounds the fp32
+// value to nearest, ties to even, and saturates at the largest finite
+// magnitude (no scaling); a load widens exactly.  NaN stays NaN.
+// ---------------------------------------------------------------------------
+struct fp8e4m3 { unsigned char b; };
+struct fp8e5m2 { unsigned char b; };
+
+// Largest finite value of a format whose largest finite encoding is MAXBITS.
+template <int MB, int BIAS, unsigned MAXBITS>
+constexpr float fp8_max_finite() {
+  float v = (float)((MAXBITS & ((1u << MB) - 1u)) | (1u << MB));
+  for (int i = 0; i < (int)(MAXBITS >> MB) - BIAS - MB; ++i) v *= 2.f;
+  return v;
+}
+
+template <int MB, int BIAS, unsigned MAXBITS>
+__device__ __forceinline__ unsigned char f32_to_fp8(float x) {
+  const unsigned u = __float_as_uint(x);
+  const unsigned char sign = (unsigned char)((u >> 24) & 0x80u);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return sign | 0x7fu;  // NaN
+  const float a = fabsf(x);
+  if (a >= fp8_max_finite<MB, BIAS, MAXBITS>()) return sign | (unsigned char)MAXBITS;  // saturate
+  if (a == 0.f) return sign;
+  constexpr int EMIN = 1 - BIAS;                  // exponent of the smallest normal
+  int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
+  if (e < EMIN) e = EMIN;                          // below: the subnormal quantum
+  // a in units of the quantum 2^(e - MB), rounded to nearest, ties to even
+  unsigned m = (unsigned)rintf(ldexpf(a, MB - e));
+  if (m >= (2u << MB)) {                           // rounding carried into the next binade
+    m >>= 1;
+    ++e;
+  }
+  unsigned bits = m < (1u << MB) ? m                                   // subnormal
+                                 : ((unsigned)(e + BIAS) << MB) | (m - (1u << MB));
+  if (bits > MAXBITS) bits = MAXBITS;
+  return sign | (unsigned char)bits;
+}
+
+template <int MB, int BIAS>
+__device__ __forceinline__ float fp8_to_f32(unsigned char b, bool e_all_ones_is_special) {
+  const unsigned E = (b & 0x7fu) >> MB, M = b & ((1u << MB) - 1u);
+  constexpr unsigned EMAX = 0x7fu >> MB;
+  float v;
+  if (E == EMAX && e_all_ones_is_special) v = M ? __builtin_nanf("") : __builtin_inff();
+  else if (E == 0) v = ldexpf((float)M, 1 - BIAS - MB);
+  else v = ldexpf((float)(M | (1u << MB)), (int)E - BIAS - MB);
+  return (b & 0x80u) ? -v : v;
+}
+
+__device__ __forceinline__ float to_f32(fp8e4m3 x) {
+  // E4M3 (no infinities): only S.1111.111 is NaN
+  return (x.b & 0x7fu) == 0x7fu ? __builtin_nanf("") : fp8_to_f32<3, 7>(x.b, false);
+}
+__device__ __forceinline__ float to_f32(fp8e5m2 x) { return fp8_to_f32<2, 15>(x.b, true); }
+template <> __device__ __forceinline__ fp8e4m3 from_f32<fp8e4m3>(float x) {
+  return fp8e4m3{f32_to_fp8<3, 7, 0x7eu>(x)};
+}
+template <> __device__ __forceinline__ fp8e5m2 from_f32<fp8e5m2>(float x) {
+  return fp8e5m2{f32_to_fp8<2, 15, 0x7bu>(x)};
+}
+
 // Matrix-core traits per compute type.
 template <typename T> struct Mfma;
 

@@ -31,7 +31,9 @@ int32_t sab_heads(const gdn_prefill_params *p) {
 
 size_t elem_size(int dtype) { return dtype == GDN_F32 ? 4 : 2; }
 
-bool valid_state_dtype(int d) { return d == GDN_F32 || d == GDN_BF16 || d == GDN_F16; }
+bool valid_state_dtype(int d) {
+  return d == GDN_F32 || d == GDN_BF16 || d == GDN_F16 || d == GDN_FP8_E4M3 || d == GDN_FP8_E5M2;
+}
 bool valid_itype(int t) { return t == GDN_I32 || t == GDN_I64; }
 
 struct Layout {

@@ -219,23 +219,18 @@ __device__ __forceinline__ bool state_runs_aligned(const void *p, const int64_t 
          (str[1] * (int64_t)sizeof(St)) % A == 0 && (str[2] * (int64_t)sizeof(St)) % A == 0;
 }
 
-template <typename St>
-struct Run4 {
-  typedef St v4 __attribute__((ext_vector_type(4)));
-};
-
 template <typename St, int D>
 __device__ __forceinline__ void write_state_t(St *p, const int64_t str[4], int64_t row, int h,
                                               int vcol, int g, const float (&S)[D / 16][4]) {
   const int64_t base = row * str[0] + (int64_t)h * str[1] + (int64_t)vcol * str[2];
   if (state_runs_aligned<St>(p, str)) {
-    typedef typename Run4<St>::v4 v4;
 #pragma unroll
     for (int it = 0; it < D / 16; ++it) {
-      v4 x;
+      St x[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[r] = from_f32<St>(S[it][r]);
-      *reinterpret_cast<v4 *>(p + base + 16 * it + 4 * g) = x;
+      __builtin_memcpy(__builtin_assume_aligned(p + base + 16 * it + 4 * g, 4 * sizeof(St)), x,
+                       sizeof(x));
     }
     return;
   }
@@ -251,7 +246,9 @@ __device__ __forceinline__ void write_state(void *base_ptr, int dtype, const int
                                          const float (&S)[D / 16][4]) {
   if (dtype == GDN_F32) write_state_t<float, D>((float *)base_ptr, str, row, h, vcol, g, S);
   else if (dtype == GDN_BF16) write_state_t<bf16, D>((bf16 *)base_ptr, str, row, h, vcol, g, S);
-  else write_state_t<_Float16, D>((_Float16 *)base_ptr, str, row, h, vcol, g, S);
+  else if (dtype == GDN_F16) write_state_t<_Float16, D>((_Float16 *)base_ptr, str, row, h, vcol, g, S);
+  else if (dtype == GDN_FP8_E4M3) write_state_t<fp8e4m3, D>((fp8e4m3 *)base_ptr, str, row, h, vcol, g, S);
+  else write_state_t<fp8e5m2, D>((fp8e5m2 *)base_ptr, str, row, h, vcol, g, S);
 }
 
 template <typename St, int D>
@@ -259,10 +256,11 @@ __device__ __forceinline__ void read_state_t(const St *p, const int64_t str[4], 
                                              int vcol, int g, float (&S)[D / 16][4]) {
   const int64_t base = row * str[0] + (int64_t)h * str[1] + (int64_t)vcol * str[2];
   if (state_runs_aligned<St>(p, str)) {
-    typedef typename Run4<St>::v4 v4;
 #pragma unroll
     for (int it = 0; it < D / 16; ++it) {
-      const v4 x = *reinterpret_cast<const v4 *>(p + base + 16 * it + 4 * g);
+      St x[4];
+      __builtin_memcpy(x, __builtin_assume_aligned(p + base + 16 * it + 4 * g, 4 * sizeof(St)),
+                       sizeof(x));
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[it][r] = to_f32(x[r]);
     }
@@ -280,7 +278,9 @@ __device__ __forceinline__ void read_state(const Args &a, bool row_ok, int64_t r
   if (a.init && row_ok) {
     if (a.init_dtype == GDN_F32) read_state_t<float, D>((const float *)a.init, a.init_str, row, h, vcol, g, S);
     else if (a.init_dtype == GDN_BF16) read_state_t<bf16, D>((const bf16 *)a.init, a.init_str, row, h, vcol, g, S);
-    else read_state_t<_Float16, D>((const _Float16 *)a.init, a.init_str, row, h, vcol, g, S);
+    else if (a.init_dtype == GDN_F16) read_state_t<_Float16, D>((const _Float16 *)a.init, a.init_str, row, h, vcol, g, S);
+    else if (a.init_dtype == GDN_FP8_E4M3) read_state_t<fp8e4m3, D>((const fp8e4m3 *)a.init, a.init_str, row, h, vcol, g, S);
+    else read_state_t<fp8e5m2, D>((const fp8e5m2 *)a.init, a.init_str, row, h, vcol, g, S);
   } else {
 #pragma unroll
     for (int it = 0; it < D / 16; ++it)

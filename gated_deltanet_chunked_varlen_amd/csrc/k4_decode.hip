@@ -66,7 +66,8 @@ template <int E>
 __device__ __forceinline__ bool state_vec_ok(const void *base, int dtype, const int64_t *str) {
   if (dtype == GDN_F32) return ColIO<float, E>::vec_ok(base, str);
   if (dtype == GDN_BF16) return ColIO<bf16, E>::vec_ok(base, str);
-  return ColIO<_Float16, E>::vec_ok(base, str);
+  if (dtype == GDN_F16) return ColIO<_Float16, E>::vec_ok(base, str);
+  return ColIO<fp8e4m3, E>::vec_ok(base, str);   // both 8-bit types: 1-byte elements
 }
 
 template <int E>
@@ -74,7 +75,9 @@ __device__ __forceinline__ void load_state_col(const void *base, int dtype, cons
                                                int64_t off, bool vec, float (&s)[E]) {
   if (dtype == GDN_F32) ColIO<float, E>::load((const float *)base + off, str[3], vec, s);
   else if (dtype == GDN_BF16) ColIO<bf16, E>::load((const bf16 *)base + off, str[3], vec, s);
-  else ColIO<_Float16, E>::load((const _Float16 *)base + off, str[3], vec, s);
+  else if (dtype == GDN_F16) ColIO<_Float16, E>::load((const _Float16 *)base + off, str[3], vec, s);
+  else if (dtype == GDN_FP8_E4M3) ColIO<fp8e4m3, E>::load((const fp8e4m3 *)base + off, str[3], vec, s);
+  else ColIO<fp8e5m2, E>::load((const fp8e5m2 *)base + off, str[3], vec, s);
 }
 
 template <int E>
@@ -82,7 +85,9 @@ __device__ __forceinline__ void store_state_col(void *base, int dtype, const int
                                                 int64_t off, bool vec, const float (&s)[E]) {
   if (dtype == GDN_F32) ColIO<float, E>::store((float *)base + off, str[3], vec, s);
   else if (dtype == GDN_BF16) ColIO<bf16, E>::store((bf16 *)base + off, str[3], vec, s);
-  else ColIO<_Float16, E>::store((_Float16 *)base + off, str[3], vec, s);
+  else if (dtype == GDN_F16) ColIO<_Float16, E>::store((_Float16 *)base + off, str[3], vec, s);
+  else if (dtype == GDN_FP8_E4M3) ColIO<fp8e4m3, E>::store((fp8e4m3 *)base + off, str[3], vec, s);
+  else ColIO<fp8e5m2, E>::store((fp8e5m2 *)base + off, str[3], vec, s);
 }
 
 // Sum over the 16 lanes of a column group.

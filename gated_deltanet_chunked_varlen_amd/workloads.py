@@ -58,6 +58,16 @@ def round_f16(x: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
 
 
+def round_fp8(x: np.ndarray, fmt: str) -> np.ndarray:
+    """fp32 values rounded to the 8-bit float format ``fmt`` ("e4m3": OCP
+    E4M3, "e5m2") by torch's CPU conversion (nearest, ties to even), returned
+    as fp32.  Used for fp8 state inputs only; values here are far inside the
+    formats' ranges."""
+    import torch
+    dt = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[fmt]
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dt).to(torch.float32).numpy()
+
+
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """fp32 -> nearest-even bf16, returned as a new fp32 array holding the
     bf16 values (finite inputs)."""
@@ -127,6 +137,7 @@ class Workload:
     in_place_pool: bool = False
     checkpoint_every: int = 0
     checkpoint_cu_starts: Optional[np.ndarray] = None
+    checkpoint_dtype: str = "f32"
     notes: dict = field(default_factory=dict)
 
     @property
@@ -162,6 +173,7 @@ def make(seed: int, lengths, hq: int, hk: int, hv: int, D: int,
          init_std: float = 0.02, init_dtype: str = "f32",
          pool_size: Optional[int] = None, in_place_pool: bool = False,
          checkpoint_every: int = 0, final_state_dtype: str = "f32",
+         checkpoint_dtype: str = "f32",
          cu_dtype=np.int32, name: str = "custom", qkv_std: float = 1.0,
          draw_lengths=None) -> Workload:
     """General seeded workload.  ``init`` is None (zero state), "seq" (one
@@ -196,6 +208,8 @@ def make(seed: int, lengths, hq: int, hk: int, hv: int, D: int,
         init_state = _round_bf16_inplace(init_state)
     if init_state is not None and init_dtype == "f16":
         init_state = round_f16(init_state)
+    if init_state is not None and init_dtype in ("e4m3", "e5m2"):
+        init_state = round_fp8(init_state, init_dtype)
     if dtype == "bf16":
         q, k, v = (_round_bf16_inplace(q), _round_bf16_inplace(k),
                    _round_bf16_inplace(v))
@@ -212,7 +226,7 @@ def make(seed: int, lengths, hq: int, hk: int, hv: int, D: int,
                     state_indices=sidx, final_state_dtype=final_state_dtype,
                     in_place_pool=in_place_pool,
                     checkpoint_every=checkpoint_every,
-                    checkpoint_cu_starts=ccs)
+                    checkpoint_cu_starts=ccs, checkpoint_dtype=checkpoint_dtype)
 
 
 # The five named workloads, seeds 1000 + index.

@@ -41,7 +41,16 @@ extern "C" {
 #define GDN_ABI_VERSION 1
 #define GDN_CHUNK 64 /* kernel chunk length in tokens */
 
-typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype;
+/* Element types.  The two 8-bit float types (OCP FP8 E4M3, max 448, and
+ * E5M2, max 57344) are for states only -- initial, final and checkpoint
+ * states (gitcode, section "chunk_gated_delta_rule API 全参数解析" lists them
+ * for initial_state, section "中间状态检查点" for state_checkpoints).  The
+ * pages give no scaling rule for them, so a state is stored by rounding each
+ * fp32 element to nearest (ties to even) with saturation at the largest
+ * finite value, and read by exact widening. */
+typedef enum {
+  GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2, GDN_FP8_E4M3 = 3, GDN_FP8_E5M2 = 4
+} gdn_dtype;
 typedef enum { GDN_I32 = 0, GDN_I64 = 1 } gdn_itype;
 
 /* Host-side error codes (return values). */
@@ -83,7 +92,7 @@ typedef enum { GDN_I32 = 0, GDN_I64 = 1 } gdn_itype;
  *   output [T, H, D] in qkv_dtype; rows outside every sequence are untouched.
  *   States are [rows, H, D(v), D(k)]: element [n][h][v][k] is S[k][v]; the
  *   four element strides are given (all zero = contiguous).  initial_state
- *   may be NULL (zero).  state dtypes: F32, BF16 or F16.
+ *   may be NULL (zero).  state dtypes: F32, BF16, F16, FP8_E4M3 or FP8_E5M2.
  *   state_indices [N] (or NULL): sequence i reads initial_state[idx[i]] and,
  *   if output_final_state, writes output_state[idx[i]]; indices must be
  *   unique (caller precondition, gitcode section "状态池"); output_state may

@@ -15,6 +15,17 @@ from oracle import oracle
 
 TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2 / 8}
 
+# A result stored in an 8-bit float state type carries, on top of the bar of
+# its computation, the rounding of every element to that format: at most the
+# format's unit roundoff relative to the element (2^-4 for E4M3 with 3
+# mantissa bits, 2^-3 for E5M2 with 2), so at most that in relative L2.
+STORE_TOL = {"e4m3": 2.0 ** -4, "e5m2": 2.0 ** -3}
+
+def state_torch_dtype(name):
+    torch = _torch()
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
+            "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[name]
+
 
 def rel_l2(x, ref):
     x = np.asarray(x, np.float64)
@@ -62,13 +73,12 @@ def _torch():
 def to_device(wl, device="cuda"):
     torch = _torch()
     qdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[wl.dtype]
-    sdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
     t = lambda a, dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dt)
     dev = dict(
         q=t(wl.q, qdt), k=t(wl.k, qdt), v=t(wl.v, qdt),
         g=t(wl.g, torch.float32), beta=t(wl.beta, torch.float32),
         cu_seqlens=torch.from_numpy(wl.cu_seqlens.copy()).to(device),
-        initial_state=t(wl.initial_state, sdt[wl.initial_state_dtype]),
+        initial_state=t(wl.initial_state, state_torch_dtype(wl.initial_state_dtype)),
         state_indices=None if wl.state_indices is None
         else torch.from_numpy(wl.state_indices.copy()).to(device),
         checkpoint_cu_starts=None if wl.checkpoint_cu_starts is None
@@ -83,7 +93,6 @@ def run_gpu(wl, device="cuda", status=False, **over):
     from gated_deltanet_chunked_varlen_amd import chunk_gated_delta_rule
     d = to_device(wl, device)
     H, D, N = wl.H, wl.D, wl.N
-    sdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
     kw = dict(g=d["g"], beta=d["beta"], scale=wl.scale,
               cu_seqlens=d["cu_seqlens"],
               use_qk_l2norm_in_kernel=wl.l2norm_in_kernel,
@@ -97,12 +106,13 @@ def run_gpu(wl, device="cuda", status=False, **over):
     else:
         kw.update(initial_state=d["initial_state"])
         if wl.output_final_state:
-            kw.update(output_state=torch.zeros((N, H, D, D), dtype=sdt[wl.final_state_dtype],
-                                               device=device))
+            kw.update(output_state=torch.zeros((N, H, D, D), dtype=torch.float32, device=device)
+                      .to(state_torch_dtype(wl.final_state_dtype)))
     ck = None
     if wl.checkpoint_every > 0:
         rows = int(wl.checkpoint_cu_starts[-1])
-        ck = torch.zeros((rows, H, D, D), dtype=torch.float32, device=device)
+        ck = torch.zeros((rows, H, D, D), dtype=torch.float32, device=device).to(
+            state_torch_dtype(wl.checkpoint_dtype))
         kw.update(state_checkpoints=ck, checkpoint_cu_starts=d["checkpoint_cu_starts"],
                   checkpoint_every_n_tokens=wl.checkpoint_every)
     st = torch.full((1,), -1, dtype=torch.int32, device=device) if status else None
@@ -138,7 +148,6 @@ def run_gpu_decode(wl, device="cuda", status=False, **over):
     assert all(int(x) == 1 for x in np.diff(wl.cu_seqlens))
     d = to_device(wl, device)
     H, D, N = wl.H, wl.D, wl.N
-    sdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
     kw = dict(g=d["g"], beta=d["beta"], scale=wl.scale,
               use_qk_l2norm_in_kernel=wl.l2norm_in_kernel,
               output_final_state=wl.output_final_state)
@@ -151,8 +160,8 @@ def run_gpu_decode(wl, device="cuda", status=False, **over):
     else:
         kw.update(initial_state=d["initial_state"])
         if wl.output_final_state:
-            kw.update(output_state=torch.zeros((N, H, D, D), dtype=sdt[wl.final_state_dtype],
-                                               device=device))
+            kw.update(output_state=torch.zeros((N, H, D, D), dtype=torch.float32, device=device)
+                      .to(state_torch_dtype(wl.final_state_dtype)))
     st = torch.full((1,), -1, dtype=torch.int32, device=device) if status else None
     if st is not None:
         kw["status"] = st
@@ -181,3 +190,12 @@ def compare(wl, gpu, orc, heads=None):
     if wl.checkpoint_every > 0 and orc["ckpt"] is not None and orc["ckpt"].size:
         errs["ckpt"] = rel_l2(sel(gpu["ckpt"]), orc["ckpt"])
     return errs, tol
+
+
+def bars(wl):
+    """The relative-L2 bar of each compared tensor: the compute bar, plus the
+    8-bit store rounding for states kept in an 8-bit float type."""
+    tol = TOL[wl.dtype]
+    return {"out": tol,
+            "final": tol + STORE_TOL.get(wl.final_state_dtype, 0.0),
+            "ckpt": tol + STORE_TOL.get(wl.checkpoint_dtype, 0.0)}

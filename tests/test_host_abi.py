@@ -126,6 +126,7 @@ def test_validate_ok_and_workspace():
     (dict(hq=4, hk=2, hv=4), "GDN_ERR_HEAD_RATIO"),
     (dict(hq=4, hk=4, hv=6), "GDN_ERR_HEAD_RATIO"),
     (dict(dtype=7), "GDN_ERR_DTYPE"),
+    (dict(dtype=3), "GDN_ERR_DTYPE"),           # 8-bit floats are for states only
     (dict(extra=dict(q=None)), "GDN_ERR_NULL"),
     (dict(extra=dict(q=ctypes.c_void_p(0x1008))), "GDN_ERR_ALIGN"),
     (dict(extra=dict(output=ctypes.c_void_p(0x1004))), "GDN_ERR_ALIGN"),
@@ -169,6 +170,23 @@ def test_validate_strides():
                                initial_state_dtype=nat.GDN_F32,
                                initial_state_strides=strides))
         assert _validate(p) == want
+
+
+def test_state_dtypes_accepted_and_rejected():
+    """All five state types are accepted for initial, final and checkpoint
+    states; anything else is GDN_ERR_DTYPE."""
+    nat = _lib()
+    for dt in (nat.GDN_F32, nat.GDN_BF16, nat.GDN_F16, nat.GDN_FP8_E4M3, nat.GDN_FP8_E5M2):
+        p = _params(extra=dict(initial_state=ctypes.c_void_p(8), initial_state_dtype=dt,
+                               output_final_state=1, output_state=ctypes.c_void_p(8),
+                               output_state_dtype=dt))
+        assert _validate(p) == 0, dt
+    for bad in (5, -1):
+        p = _params(extra=dict(initial_state=ctypes.c_void_p(8), initial_state_dtype=bad))
+        assert _validate(p) == code("GDN_ERR_DTYPE")
+        p = _params(extra=dict(output_final_state=1, output_state=ctypes.c_void_p(8),
+                               output_state_dtype=bad))
+        assert _validate(p) == code("GDN_ERR_DTYPE")
 
 
 def test_workspace_size_zero_for_bad_shape():
