@@ -81,46 +81,6 @@ struct RegOps {
   __device__ __forceinline__ float glog() const { return op.glog; }
 };
 
-// ... or read from an LDS slot laid out like the workspace blocks:
-// [W fragments][Ktilde fragments][U tiles of the group][G_last].
-template <typename T, int D, int NCW>
-struct SlotGeo {
-  static constexpr int E = sizeof(T);
-  static constexpr int W_BYTES = 64 * D * E;
-  static constexpr int U_TILE_BYTES = 4 * 64 * 4 * E;
-  static constexpr int K_OFF = W_BYTES;
-  static constexpr int U_OFF = 2 * W_BYTES;
-  static constexpr int G_OFF = U_OFF + NCW * U_TILE_BYTES;
-  static constexpr int BYTES = (G_OFF + 4 + 15) / 16 * 16;
-  static constexpr int NV_W = W_BYTES / (64 * 16);        // 16-byte loads per lane
-  static constexpr int NV_U = NCW * U_TILE_BYTES / (64 * 16);
-  static constexpr int NV = 2 * NV_W + NV_U;
-};
-
-template <typename T, int D, int NCW>
-struct LdsOps {
-  static constexpr bool kInterleave = true;
-  typedef typename Mfma<T>::frag frag;
-  static constexpr int KPL = Mfma<T>::KPL, KS_D = Geo<T, D>::KS_D, KS_C = Geo<T, D>::KS_C;
-  const unsigned char *slot;
-  int lane, cw;
-  __device__ __forceinline__ frag w(int it, int kt) const {
-    return *reinterpret_cast<const frag *>(slot + (((it * KS_D + kt) * 64 + lane) * KPL) * sizeof(T));
-  }
-  __device__ __forceinline__ frag k(int it, int kt) const {
-    return *reinterpret_cast<const frag *>(slot + SlotGeo<T, D, NCW>::K_OFF +
-                                           (((it * KS_C + kt) * 64 + lane) * KPL) * sizeof(T));
-  }
-  __device__ __forceinline__ f32x4 uvec(int it) const {
-    const T *up = reinterpret_cast<const T *>(slot + SlotGeo<T, D, NCW>::U_OFF) +
-                  ((cw * 4 + it) * 64 + lane) * 4;
-    return f32x4{to_f32(up[0]), to_f32(up[1]), to_f32(up[2]), to_f32(up[3])};
-  }
-  __device__ __forceinline__ float glog() const {
-    return *reinterpret_cast<const float *>(slot + SlotGeo<T, D, NCW>::G_OFF);
-  }
-};
-
 // One chunk of the state recurrence for one lane's share of a 16-column tile.
 // With xb non-null (the fused state/output pass) the chunk-start state and
 // N fragments go to that LDS buffer instead of the workspace: KS_D state
@@ -404,14 +364,17 @@ __device__ __forceinline__ void dma4(const void *src, unsigned char *dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 4, 0, 0);
 }
 
-// One LDS slot of the fused pass: [W][Ktilde][U tile][gate row (64 floats)].
+// One LDS slot of the fused pass, laid out like the workspace blocks:
+// [W fragments][Ktilde fragments][the tile's U][gate row (64 floats)].
 template <typename T, int D>
 struct DmaSlotGeo {
-  using CS = SlotGeo<T, D, 1>;
-  static constexpr int K_OFF = CS::K_OFF, U_OFF = CS::U_OFF;
-  static constexpr int G_OFF = CS::U_OFF + CS::U_TILE_BYTES;
+  static constexpr int W_BYTES = 64 * D * (int)sizeof(T);
+  static constexpr int U_TILE_BYTES = 4 * 64 * 4 * (int)sizeof(T);   // 64 rows x 16 columns
+  static constexpr int K_OFF = W_BYTES, U_OFF = 2 * W_BYTES;
+  static constexpr int G_OFF = U_OFF + U_TILE_BYTES;
   static constexpr int BYTES = G_OFF + 64 * 4;
-  static constexpr int NP = CS::NV;            // 1 KB pieces (W, Ktilde, U)
+  static constexpr int NV_W = W_BYTES / 1024;                         // 1 KB pieces per block
+  static constexpr int NP = 2 * NV_W + U_TILE_BYTES / 1024;          // pieces (W, Ktilde, U)
 };
 
 template <typename T, int D>
@@ -442,7 +405,7 @@ struct DmaSlotOps {
 template <typename T, int D, int NLD>
 struct DmaLoader {
   using SG = DmaSlotGeo<T, D>;
-  static constexpr int NV_W = SG::CS::NV_W;
+  static constexpr int NV_W = SG::NV_W;
   static constexpr int64_t BLK = Geo<T, D>::W_ELEMS * sizeof(T) / 16;   // u32x4 per 64 x D block
   static constexpr int NPC = SG::NP + 1;                                 // loads per chunk
   static constexpr int PPW = (SG::NP + NLD - 1) / NLD;
@@ -484,7 +447,7 @@ struct L2Warm {
   static constexpr int WL = Geo<T, D>::W_ELEMS * (int)sizeof(T) / LINE;  // lines per 64 x D block
   static constexpr int PL = 64 * 64 * (int)sizeof(T) / LINE;             // lines per P block
   static constexpr int SHARED = 3 * WL + PL;
-  static constexpr int UL = SlotGeo<T, D, 1>::U_TILE_BYTES / LINE;
+  static constexpr int UL = DmaSlotGeo<T, D>::U_TILE_BYTES / LINE;
   static constexpr int GL = 64 * 4 / LINE;
 
   __device__ __forceinline__ static void touch(const Args &a, int64_t ch, int jg, int lane,
@@ -504,7 +467,7 @@ struct L2Warm {
       dma4(src, junk);
     }
     const unsigned char *uf = (const unsigned char *)a.Uf + ch * (WL * LINE) +
-                              (int64_t)jg * SlotGeo<T, D, 1>::U_TILE_BYTES;
+                              (int64_t)jg * DmaSlotGeo<T, D>::U_TILE_BYTES;
     const unsigned char *gw = (const unsigned char *)(a.Gw + ch * kChunk);
     const int l = min(lane, UL + GL - 1);
     dma4(l < UL ? uf + l * LINE : gw + (l - UL) * LINE, junk);
@@ -714,7 +677,7 @@ state_output_kernel(Args a) {
     wait_vm<0>();
   } else {
     // ---------------- loader waves ------------------------------------------
-    const LD ld{(int64_t)jg * (SG::CS::U_TILE_BYTES / 16), lane, wave - 1};
+    const LD ld{(int64_t)jg * (SG::U_TILE_BYTES / 16), lane, wave - 1};
     for (int cc = 0; cc < AHEAD && cc < nc; ++cc) ld.issue(a, ch0 + (int64_t)cc, cslots[cc]);
     for (int st = 0; st <= nc + 1; ++st) {
       __builtin_amdgcn_s_barrier();
