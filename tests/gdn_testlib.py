@@ -15,11 +15,13 @@ from oracle import oracle
 
 TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2 / 8}
 
-# A result stored in an 8-bit float state type carries, on top of the bar of
-# its computation, the rounding of every element to that format: at most the
-# format's unit roundoff relative to the element (2^-4 for E4M3 with 3
-# mantissa bits, 2^-3 for E5M2 with 2), so at most that in relative L2.
-STORE_TOL = {"e4m3": 2.0 ** -4, "e5m2": 2.0 ** -3}
+# A state stored in a narrower type than fp32 carries, on top of the bar of
+# its computation, the rounding of every element to that type: at most the
+# type's unit roundoff relative to the element (2^-8 bf16, 2^-11 fp16, 2^-4
+# E4M3 with 3 mantissa bits, 2^-3 E5M2 with 2), so at most that in relative
+# L2.
+STORE_TOL = {"f32": 0.0, "bf16": 2.0 ** -8, "f16": 2.0 ** -11,
+             "e4m3": 2.0 ** -4, "e5m2": 2.0 ** -3}
 
 def state_torch_dtype(name):
     torch = _torch()
@@ -194,7 +196,7 @@ def compare(wl, gpu, orc, heads=None):
 
 def bars(wl):
     """The relative-L2 bar of each compared tensor: the compute bar, plus the
-    8-bit store rounding for states kept in an 8-bit float type."""
+    store rounding for states kept in a type narrower than fp32."""
     tol = TOL[wl.dtype]
     return {"out": tol,
             "final": tol + STORE_TOL.get(wl.final_state_dtype, 0.0),
