@@ -386,9 +386,9 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
-            print("bench.py: this build runs on one GPU only (the state pass "
-                  "shards by sequence and head without communication; see the "
-                  "design notes); --gpus %d is not supported" % args.gpus,
+            print("bench.py: the library runs on one GPU only (more GPUs would "
+                  "take whole sequences or heads each, with no communication); "
+                  "--gpus %d is not supported" % args.gpus,
                   file=sys.stderr)
         sys.exit(2)
 
