@@ -291,6 +291,7 @@ static void fill_args(const gdn_prefill_params *p, const Layout *L, int num_cus,
       const int64_t inter = gdn_max_chunks(p->total_tokens, p->num_seqs) * H *
                             (4 * 64 * D + 64 * 64) * 2;
       a.warm = inter > kWarmBytes ? 2 : 0;
+      a.nt_stores = inter > kWarmBytes ? 1 : 0;
     } else {
       a.Hf = ws + L->Hf;
       a.Nf = ws + L->Nf;

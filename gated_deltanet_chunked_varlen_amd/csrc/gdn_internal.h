@@ -71,6 +71,11 @@ struct Args {
   // one wave pulls into L2 (0: off; set when the intermediates outgrow the
   // last-level cache and the pass would read them from HBM)
   int32_t warm;
+  // 16-bit intra-chunk pass, set with warm: write the intermediates with
+  // non-temporal stores.  They then outgrow the last-level cache and are read
+  // back from HBM anyway; below that size plain stores leave them in the
+  // last-level cache for the state pass.
+  int32_t nt_stores;
 };
 
 #ifdef __HIPCC__

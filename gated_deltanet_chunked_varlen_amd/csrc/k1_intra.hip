@@ -295,6 +295,15 @@ static hipError_t launch_intra_t(const Args &a, hipStream_t s) {
 // workgroups share a CU.  The chunk's first token and length come from the
 // (first token, length) table in one load.
 // ---------------------------------------------------------------------------
+// A store of an intermediate: non-temporal when the intermediates outgrow the
+// last-level cache (NT), plain otherwise.  NT is a template parameter: with a
+// run-time flag the compiler merges the two stores and drops the hint.
+template <bool NT, typename V>
+__device__ __forceinline__ void st_inter(V *p, const V &v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 template <typename T, int D>
 struct IntraSmemB {
   static constexpr int LDK = D + 16;  // row pitch in elements (32 B pad)
@@ -302,7 +311,7 @@ struct IntraSmemB {
   float AT[64][68];                   // A, then T; [t][64] = G, [t][65] = beta
 };
 
-template <typename T, int D>
+template <typename T, int D, bool NTS>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) intra_kernel_h(Args a) {
   using M = Mfma<T>;
   typedef typename M::frag frag;
@@ -407,13 +416,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
 #pragma unroll
     for (int kt = 0; kt < KS_C; ++kt)
       if (2 * kt <= tt)
-        *reinterpret_cast<frag *>(pf_out + (((int64_t)tt * KS_C + kt) * 64 + lane) * 8) = pf[kt];
+        st_inter<NTS>(reinterpret_cast<frag *>(pf_out + (((int64_t)tt * KS_C + kt) * 64 + lane) * 8), pf[kt]);
 #pragma unroll
     for (int kt = 0; kt < KS_D; ++kt) {
       frag qf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[e] = QR[t][pi_idx(g, kt * 8 + e)];
-      *reinterpret_cast<frag *>(qf_out + (((int64_t)tt * KS_D + kt) * 64 + lane) * 8) = qf;
+      st_inter<NTS>(reinterpret_cast<frag *>(qf_out + (((int64_t)tt * KS_D + kt) * 64 + lane) * 8), qf);
     }
     lds_sync();  // q is consumed: A may overwrite the buffer
   }
@@ -530,7 +539,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
     }
 #pragma unroll
     for (int kt = 0; kt < KS_D; ++kt)
-      *reinterpret_cast<frag *>(wf + ((int64_t)kt * 64 + lane) * 8) = out[kt];
+      st_inter<NTS>(reinterpret_cast<frag *>(wf + ((int64_t)kt * 64 + lane) * 8), out[kt]);
   }
   // ---- Ktilde^T fragments: rows pi(g, 8kt + e) of k column 16 it2 + c ------
   {
@@ -548,7 +557,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
         const int j = (e < 4 ? r0 : r1) + (e & 3);
         y[e] = (float)kv[e] * gexp(glast - AT[j][64]);
       }
-      *reinterpret_cast<frag *>(kf + ((int64_t)fidx * 64 + lane) * 8) = M::pack(y);
+      st_inter<NTS>(reinterpret_cast<frag *>(kf + ((int64_t)fidx * 64 + lane) * 8), M::pack(y));
     }
   }
   lds_sync();  // k rows consumed
@@ -581,25 +590,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
       typename M::half o4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) o4[r] = (T)acc[r];
-      *reinterpret_cast<typename M::half *>(dst) = o4;
+      st_inter<NTS>(reinterpret_cast<typename M::half *>(dst), o4);
     }
   }
 }
 
-template <typename T, int D>
-static hipError_t launch_intra_h(const Args &a, hipStream_t s) {
+template <typename T, int D, bool NTS>
+static hipError_t launch_intra_h_nt(const Args &a, hipStream_t s) {
   const size_t smem = sizeof(IntraSmemB<T, D>);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)intra_kernel_h<T, D>,
+    hipError_t e = hipFuncSetAttribute((const void *)intra_kernel_h<T, D, NTS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t blocks = a.cap * a.H;
   if (blocks == 0) return hipSuccess;
-  intra_kernel_h<T, D><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
+  intra_kernel_h<T, D, NTS><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_intra_h(const Args &a, hipStream_t s) {
+  return a.nt_stores ? launch_intra_h_nt<T, D, true>(a, s) : launch_intra_h_nt<T, D, false>(a, s);
 }
 
 hipError_t launch_intra(const Args &a, hipStream_t s) {
