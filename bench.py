@@ -145,6 +145,24 @@ def load_traffic(phase, workload):
     return rec.get("bytes_per_launch")
 
 
+def load_mfma(workload):
+    """rocprofv3-measured matrix-core use per phase from the committed counter
+    summary (profiles/mfma.json), for phases whose kernel source is
+    unchanged since the counters were taken; {} if none."""
+    path = os.path.join(ROOT, "profiles", "mfma.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        db = json.load(f)
+    res = {}
+    for ph in PHASES:
+        rec = db.get("%s/%s" % (ph, workload))
+        if rec and rec.get("source_hash") == source_hash(KERNEL_SOURCES[ph]):
+            res[ph] = {"mfma_busy_frac": rec["mfma_busy_frac"],
+                       "bf16_tflop_per_launch": rec["bf16_flop_per_launch"] / 1e12}
+    return res
+
+
 def cpu_baseline(wl, seconds):
     """The oracle as it stands, timed on this host: the whole workload,
     repeated until ``seconds`` have passed (at least once)."""
@@ -281,6 +299,50 @@ def summarize(argv):
     print(out)
 
 
+def summarize_mfma(argv):
+    """Write profiles/<workload>_mfma.md and update profiles/mfma.json from a
+    rocprofv3 --pmc run with SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE,
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 and SQ_BUSY_CU_CYCLES: argv = workload,
+    counter dir, command text.  Matrix-core busy fraction = busy cycles summed
+    over the SIMDs / (GPU-active cycles of one XCD x 1024 SIMDs), the form of
+    rocprofv3's own MfmaUtil metric; GRBM_GUI_ACTIVE arrives summed over the 8
+    XCDs.  Executed bf16/fp16 matrix FLOP = MOPS x 512."""
+    import collections
+    import csv
+    wname, cdir = argv[:2]
+    cmd = " ".join(argv[2:])
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(_one(cdir, "*counter_collection.csv"))):
+        ph = _phase_of(r["Kernel_Name"])
+        if ph:
+            per[ph][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    avg = lambda v: sum(v) / len(v)
+    lines = ["# Matrix-core counters: %s" % wname, "",
+             "Command:", "", "    " + cmd, "",
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
+             "executed matrix FLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (fp16 inputs count "
+             "under F16 and read 0 here). Counter runs serialise and lengthen kernels, so the "
+             "busy fraction is a lower bound on the unprofiled one.", "",
+             "| kernel | dispatches | MFMA busy | executed matrix GFLOP per launch |",
+             "|---|---|---|---|"]
+    db_path = os.path.join(ROOT, "profiles", "mfma.json")
+    db = json.load(open(db_path)) if os.path.exists(db_path) else {}
+    for ph in PHASES + ["decode"]:
+        c = per.get(ph)
+        if not c or "SQ_VALU_MFMA_BUSY_CYCLES" not in c or "GRBM_GUI_ACTIVE" not in c:
+            continue
+        busy = avg(c["SQ_VALU_MFMA_BUSY_CYCLES"]) / (avg(c["GRBM_GUI_ACTIVE"]) / 8.0 * 1024.0)
+        flop = avg(c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0.0])) * 512.0
+        lines.append("| %s | %d | %.2f%% | %.3f |" % (
+            ph, len(c["SQ_VALU_MFMA_BUSY_CYCLES"]), 100.0 * busy, flop / 1e9))
+        db["%s/%s" % (ph, wname)] = {"mfma_busy_frac": busy, "bf16_flop_per_launch": flop,
+                                     "source_hash": source_hash(KERNEL_SOURCES[ph])}
+    json.dump(db, open(db_path, "w"), indent=1, sort_keys=True)
+    out = os.path.join(ROOT, "profiles", "%s_mfma.md" % wname)
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
 def bench_decode(args):
     """The decode step on the decode workload: one JSON line of its own."""
     import torch
@@ -369,6 +431,9 @@ def bench_decode(args):
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
         summarize(sys.argv[2:])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-mfma":
+        summarize_mfma(sys.argv[2:])
         return
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -524,6 +589,7 @@ def main():
         "tflops_canonical": tflops,
         "mfma_peak_frac": tflops / peak_mm,
         "phase_ms_warmup": phase_ms,
+        "mfma_counters": load_mfma(wl.name) or None,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "avg_launch_ms": dom_ms,
