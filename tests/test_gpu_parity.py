@@ -342,6 +342,30 @@ def test_c4_gva_checkpoints():
     _check(wl, gpu, orc, heads=heads)
 
 
+# Calls whose intermediates outgrow the 256 MB last-level cache take the
+# large-call form: non-temporal intermediate stores and the L2 warm-up wave of
+# the state pass.  The configs above reach it only at D = 128; these two reach
+# it at D = 64 (fp16, in-kernel norm, in-place pool, checkpoints) and at D = 32
+# (bf16, no norm, GQA), checked on every head.
+@pytest.mark.timeout(600)
+def test_large_call_form_d64_f16_pool_checkpoints():
+    wl = W.make(31, [5000, 4000, 4500], 16, 16, 16, 64, "f16", l2norm_in_kernel=True,
+                init="pool", pool_size=7, in_place_pool=True, checkpoint_every=1024,
+                name="large_d64_f16")
+    gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] == 0
+    _check(wl, gpu, tl.run_oracle(wl))
+
+
+@pytest.mark.timeout(600)
+def test_large_call_form_d32_bf16_gqa():
+    wl = W.make(32, [6100, 130, 4990], 32, 8, 8, 32, "bf16", normalise_in_generator=True,
+                init="seq", name="large_d32_bf16")
+    gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] == 0
+    _check(wl, gpu, tl.run_oracle(wl))
+
+
 @pytest.mark.timeout(600)
 def test_c5_long_single_sampled_heads():
     wl = W.c5_long_single()
