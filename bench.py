@@ -85,6 +85,9 @@ def per_token_head_bytes(wl, phase):
 
 
 FLOPS_PER_TOKEN_HEAD = lambda D: 2 * (5 * 64 * D + 3 * D * D)   # eight chunk GEMMs
+# the same with the five products that involve a 64 x 64 triangle (K K^T,
+# Q K^T, T (beta gamma K), T (beta V), P N) counted at half a tile
+FLOPS_TRI_PER_TOKEN_HEAD = lambda D: 2 * (5 * 32 * D + 3 * D * D)
 
 
 def decode_bytes_per_seq_head(wl):
@@ -587,6 +590,7 @@ def main():
                    "head_size": D, "qk_l2norm_in_kernel": wl.l2norm_in_kernel,
                    "parallelism": "single GPU"},
         "tflops_canonical": tflops,
+        "tflops_triangle": T * H * FLOPS_TRI_PER_TOKEN_HEAD(D) / (ms_step / 1e3) / 1e12,
         "mfma_peak_frac": tflops / peak_mm,
         "phase_ms_warmup": phase_ms,
         "mfma_counters": load_mfma(wl.name) or None,
