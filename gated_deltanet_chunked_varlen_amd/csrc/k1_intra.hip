@@ -28,10 +28,11 @@ namespace gdn {
 
 template <typename T> struct Pad { static constexpr int v = 16 / sizeof(T); };
 
-// LDS plan (about 53 KB for bf16 at D = 128, so three workgroups share a CU):
-// k rows are needed only for K K^T, v (transposed) only after it, so they
-// share storage; A is inverted in place into T; the two spare columns of the
-// padded A/T rows hold G and beta.
+// LDS plan of the fp32 variant (intra_kernel; 16-bit inputs take
+// intra_kernel_h below): about 85 KB at D = 128, one workgroup per CU.  k rows
+// are needed only for K K^T, v (transposed) only after it, so they share
+// storage; A is inverted in place into T; the two spare columns of the padded
+// A/T rows hold G and beta.
 template <typename T, int D>
 struct IntraSmem {
   union {
