@@ -366,25 +366,28 @@ __device__ __forceinline__ void dma4(const void *src, unsigned char *dst) {
 
 // One LDS slot of the fused pass, laid out like the workspace blocks:
 // [W fragments][Ktilde fragments][the tile's U][gate row (64 floats)].
-template <typename T, int D>
+// TW = 1 or 2 column tiles per workgroup: their U tiles sit side by side
+// (adjacent in the workspace too).
+template <typename T, int D, int TW = 1>
 struct DmaSlotGeo {
   static constexpr int W_BYTES = 64 * D * (int)sizeof(T);
   static constexpr int U_TILE_BYTES = 4 * 64 * 4 * (int)sizeof(T);   // 64 rows x 16 columns
   static constexpr int K_OFF = W_BYTES, U_OFF = 2 * W_BYTES;
-  static constexpr int G_OFF = U_OFF + U_TILE_BYTES;
+  static constexpr int G_OFF = U_OFF + TW * U_TILE_BYTES;
   static constexpr int BYTES = G_OFF + 64 * 4;
   static constexpr int NV_W = W_BYTES / 1024;                         // 1 KB pieces per block
-  static constexpr int NP = 2 * NV_W + U_TILE_BYTES / 1024;          // pieces (W, Ktilde, U)
+  static constexpr int NP = 2 * NV_W + TW * U_TILE_BYTES / 1024;     // pieces (W, Ktilde, U)
 };
 
-template <typename T, int D>
+template <typename T, int D, int TW = 1>
 struct DmaSlotOps {
   static constexpr bool kInterleave = true;
   typedef typename Mfma<T>::frag frag;
-  using SG = DmaSlotGeo<T, D>;
+  using SG = DmaSlotGeo<T, D, TW>;
   static constexpr int KPL = Mfma<T>::KPL, KS_D = Geo<T, D>::KS_D, KS_C = Geo<T, D>::KS_C;
   const unsigned char *slot;
   int lane;
+  int utile;  // which of the slot's U tiles
   __device__ __forceinline__ frag w(int it, int kt) const {
     return *reinterpret_cast<const frag *>(slot + (((it * KS_D + kt) * 64 + lane) * KPL) * sizeof(T));
   }
@@ -392,7 +395,8 @@ struct DmaSlotOps {
     return *reinterpret_cast<const frag *>(slot + SG::K_OFF + (((it * KS_C + kt) * 64 + lane) * KPL) * sizeof(T));
   }
   __device__ __forceinline__ f32x4 uvec(int it) const {
-    const T *up = reinterpret_cast<const T *>(slot + SG::U_OFF) + (it * 64 + lane) * 4;
+    const T *up = reinterpret_cast<const T *>(slot + SG::U_OFF + utile * SG::U_TILE_BYTES) +
+                  (it * 64 + lane) * 4;
     return f32x4{to_f32(up[0]), to_f32(up[1]), to_f32(up[2]), to_f32(up[3])};
   }
   __device__ __forceinline__ float glog() const {
@@ -402,9 +406,9 @@ struct DmaSlotOps {
 
 // Loader wave `part` of NLD: its share of a chunk's pieces (piece i goes to
 // part i % NLD; the gate row, one 4-byte-per-lane load, to the last part).
-template <typename T, int D, int NLD>
+template <typename T, int D, int NLD, int TW = 1>
 struct DmaLoader {
-  using SG = DmaSlotGeo<T, D>;
+  using SG = DmaSlotGeo<T, D, TW>;
   static constexpr int NV_W = SG::NV_W;
   static constexpr int64_t BLK = Geo<T, D>::W_ELEMS * sizeof(T) / 16;   // u32x4 per 64 x D block
   static constexpr int NPC = SG::NP + 1;                                 // loads per chunk
@@ -440,25 +444,28 @@ struct DmaLoader {
 // (sequence, head) share one XCD's L2 (consecutive ids map round-robin onto
 // the 8 XCDs), so each touches every NT-th line of the shared W, Ktilde, q
 // and P blocks, plus its own U tile and the gate row.
-template <typename T, int D>
+template <typename T, int D, int TW = 1>
 struct L2Warm {
-  static constexpr int NT = D / 16;
+  static constexpr int NWG = D / 16 / TW;  // workgroups per (sequence, head)
   static constexpr int LINE = 128;
   static constexpr int WL = Geo<T, D>::W_ELEMS * (int)sizeof(T) / LINE;  // lines per 64 x D block
   static constexpr int PL = 64 * 64 * (int)sizeof(T) / LINE;             // lines per P block
   static constexpr int SHARED = 3 * WL + PL;
-  static constexpr int UL = DmaSlotGeo<T, D>::U_TILE_BYTES / LINE;
+  static constexpr int UL = TW * DmaSlotGeo<T, D>::U_TILE_BYTES / LINE;  // this workgroup's U
   static constexpr int GL = 64 * 4 / LINE;
+  static_assert(UL + GL <= 64, "one line per lane");
 
-  __device__ __forceinline__ static void touch(const Args &a, int64_t ch, int jg, int lane,
+  // jw: this workgroup's index among the NWG of its (sequence, head); its
+  // tiles are TW jw .. TW jw + TW - 1
+  __device__ __forceinline__ static void touch(const Args &a, int64_t ch, int jw, int lane,
                                                unsigned char *junk) {
     const unsigned char *wf = (const unsigned char *)a.Wf + ch * (WL * LINE);
     const unsigned char *kf = (const unsigned char *)a.Kf + ch * (WL * LINE);
     const unsigned char *qf = (const unsigned char *)a.Qf + ch * (WL * LINE);
     const unsigned char *pf = (const unsigned char *)a.Pf + ch * (PL * LINE);
 #pragma unroll
-    for (int l0 = 0; l0 < SHARED; l0 += NT * 64) {
-      const int l = l0 + jg + NT * lane;
+    for (int l0 = 0; l0 < SHARED; l0 += NWG * 64) {
+      const int l = l0 + jw + NWG * lane;
       const int lc = min(l, SHARED - 1);
       const unsigned char *src = lc < WL ? wf + lc * LINE
                                : lc < 2 * WL ? kf + (lc - WL) * LINE
@@ -467,7 +474,7 @@ struct L2Warm {
       dma4(src, junk);
     }
     const unsigned char *uf = (const unsigned char *)a.Uf + ch * (WL * LINE) +
-                              (int64_t)jg * DmaSlotGeo<T, D>::U_TILE_BYTES;
+                              (int64_t)jw * TW * DmaSlotGeo<T, D>::U_TILE_BYTES;
     const unsigned char *gw = (const unsigned char *)(a.Gw + ch * kChunk);
     const int l = min(lane, UL + GL - 1);
     dma4(l < UL ? uf + l * LINE : gw + (l - UL) * LINE, junk);
@@ -558,42 +565,72 @@ __device__ __forceinline__ void output_regs(const Args &a, const OutRegs<T, D> &
 
 // One step of an output wave (st >= 2): fetch chunk st into `into` (past
 // the last chunk it repeats the last chunk), then output chunk st - 2 from
-// `proc`, fetched two steps earlier.  The step loop below runs whole rounds
-// of the three-deep ring without conditions, so the compiler's wait for
-// `proc` counts exactly the loads issued after it.
-template <typename T, int D>
+// `proc`, fetched two steps earlier, for each of the workgroup's TW column
+// tiles (jg0, jg0 + 1, ...).  The step loop below runs whole rounds of the
+// three-deep ring without conditions, so the compiler's wait for `proc`
+// counts exactly the loads issued after it.
+template <typename T, int D, int TW>
 __device__ __forceinline__ void output_wave_step(const Args &a, int st, int nc, int len, int sbos,
-                                                 int64_t ch0, int jg, int h, int lane, int ow,
+                                                 int64_t ch0, int jg0, int h, int lane, int ow,
                                                  OutRegs<T, D> &into, const OutRegs<T, D> &proc,
-                                                 const typename Mfma<T>::frag (*xbuf)[(Geo<T, D>::KS_D + Geo<T, D>::KS_C) * 64]) {
+                                                 const typename Mfma<T>::frag (*xbuf)[2][(Geo<T, D>::KS_D + Geo<T, D>::KS_C) * 64]) {
   lds_sync();
   into.issue(a, ch0 + (int64_t)min(st, nc - 1), lane, ow);
   const int oc = st - 2;
-  output_regs<T, D>(a, proc, xbuf[oc & 1], jg, (int64_t)sbos + (int64_t)kChunk * oc,
-                    min(kChunk, len - kChunk * oc), h, lane, ow);
+#pragma unroll
+  for (int t = 0; t < TW; ++t)
+    output_regs<T, D>(a, proc, xbuf[t][oc & 1], jg0 + t, (int64_t)sbos + (int64_t)kChunk * oc,
+                      min(kChunk, len - kChunk * oc), h, lane, ow);
 }
 
-constexpr int kFusedOutWaves = 2, kFusedLoadWaves = 2, kFusedWarmWaves = 1, kFusedSlots = 4;
+constexpr int kFusedOutWaves = 2, kFusedLoadWaves = 2;
 
-template <typename T, int D>
-__global__ void __launch_bounds__(64 * (1 + kFusedOutWaves + kFusedLoadWaves + kFusedWarmWaves))
+// Waves of the fused pass: TW = 1 as in the header comment (six waves); TW = 2
+// (eight): compute waves 0 and 2 (one per column tile), output waves 1 and 3
+// (each for both tiles), L2 warm-up wave 4, loaders 5 and 7, and wave 6 only
+// keeps the step barriers.  Waves are dealt to the CU's four SIMDs in turn
+// (wave w on SIMD w % 4), so each SIMD holds one matrix-core-heavy wave and
+// one light one.
+template <int TW> struct FusedRoles;
+template <> struct FusedRoles<1> {
+  static constexpr int kWaves = 6, kSlots = 4, kWarm = 4;
+  __device__ static int compute_tile(int w) { return w == 0 ? 0 : -1; }
+  __device__ static int out_index(int w) { return w == 3 ? 0 : w == 5 ? 1 : -1; }
+  __device__ static int loader_part(int w) { return w == 1 ? 0 : w == 2 ? 1 : -1; }
+};
+template <> struct FusedRoles<2> {
+  static constexpr int kWaves = 8, kSlots = 3, kWarm = 4;
+  __device__ static int compute_tile(int w) { return w == 0 ? 0 : w == 2 ? 1 : -1; }
+  __device__ static int out_index(int w) { return w == 1 ? 0 : w == 3 ? 1 : -1; }
+  __device__ static int loader_part(int w) { return w == 5 ? 0 : w == 7 ? 1 : -1; }
+};
+
+// TW column tiles per workgroup.  TW = 2 shares the workgroup's W / Ktilde
+// loads and its output waves' q / P loads between two tiles, which halves the
+// operand traffic per column; it needs a three-slot ring (one chunk ahead
+// instead of two) to fit LDS, and is used when the one-tile grid does not fit
+// on the CUs at once, so that traffic, not the chain, bounds the pass.
+template <typename T, int D, int TW>
+__global__ void __launch_bounds__(64 * FusedRoles<TW>::kWaves)
 state_output_kernel(Args a) {
-  constexpr int NT = D / 16, NLD = kFusedLoadWaves, NSLOT = kFusedSlots;
+  using R = FusedRoles<TW>;
+  constexpr int NT = D / 16, NWG = NT / TW, NLD = kFusedLoadWaves, NSLOT = R::kSlots;
   constexpr int AHEAD = NSLOT - 2;     // chunks the loaders run ahead
-  using SG = DmaSlotGeo<T, D>;
-  using LD = DmaLoader<T, D, NLD>;
+  using SG = DmaSlotGeo<T, D, TW>;
+  using LD = DmaLoader<T, D, NLD, TW>;
   typedef typename Mfma<T>::frag frag;
   constexpr int XB = Geo<T, D>::KS_D + Geo<T, D>::KS_C;  // fragments per chunk in xbuf
-  static_assert(AHEAD == 2, "the loader waits below assume two chunks ahead");
+  static_assert(AHEAD == 1 || AHEAD == 2, "the loader waits below handle one or two chunks ahead");
   static_assert(AHEAD * LD::MIN_PER_PART <= 63, "vmcnt range");
-  static_assert(kFusedWarmWaves == 1, "one warm-up wave");
+  static_assert(NT % TW == 0, "whole tiles per workgroup");
   __shared__ __align__(16) unsigned char cslots[NSLOT][SG::BYTES];
-  __shared__ frag xbuf[2][XB * 64];
+  __shared__ frag xbuf[TW][2][XB * 64];
   __shared__ __align__(16) unsigned char junk[256];
 
   const int b = blockIdx.x;
-  const int jg = (b >> 3) % NT;
-  const int u = (b / (8 * NT)) * 8 + (b & 7);
+  const int jw = (b >> 3) % NWG;       // workgroup within its (sequence, head)
+  const int jg0 = jw * TW;             // first column tile
+  const int u = (b / (8 * NWG)) * 8 + (b & 7);
   const int H = a.H;
   if (u >= a.N * H) return;
   const int seq = u / H, h = u % H;
@@ -604,15 +641,10 @@ state_output_kernel(Args a) {
   seq_geometry(a, seq, lane, f0, nc, len, sbos);
   const int64_t ch0 = ws_index(f0, h, a.cap);
 
-  // Roles by wave index.  Waves are dealt to the CU's four SIMDs in turn
-  // (wave w on SIMD w % 4), so the compute wave (0) shares its SIMD with the
-  // light warm-up wave (4), and each loader / output wave gets a SIMD whose
-  // other wave does not issue matrix-core work on the critical path.
-  static_assert(1 + kFusedOutWaves + NLD + kFusedWarmWaves == 6, "six waves");
-  constexpr int kWarmWave = 4;
-  const bool is_out = wave == 3 || wave == 5;
-  if (wave == 0) {
-    // ---------------- compute wave ------------------------------------------
+  const int ct = R::compute_tile(wave), ow = R::out_index(wave), part = R::loader_part(wave);
+  if (ct >= 0) {
+    // ---------------- compute wave (column tile jg0 + ct) --------------------
+    const int jg = jg0 + ct;
     const int vcol = 16 * jg + c;
     int64_t row = seq;
     bool row_ok = true;
@@ -627,8 +659,8 @@ state_output_kernel(Args a) {
       lds_sync();
       if (st == 0 || st > nc) continue;
       const int cc = st - 1;
-      const DmaSlotOps<T, D> op{cslots[cc % NSLOT], lane};
-      chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[cc & 1]);
+      const DmaSlotOps<T, D, TW> op{cslots[cc % NSLOT], lane, ct};
+      chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[ct][cc & 1]);
       if (a.ck_every > 0) {
         const int done = (cc + 1) * kChunk;
         if (done <= len && done % a.ck_every == 0) {
@@ -640,9 +672,8 @@ state_output_kernel(Args a) {
     }
     if (a.out_final && a.outst && row_ok)
       write_state<T, D>(a.outst, a.out_dtype, a.out_str, row, h, vcol, g, S);
-  } else if (is_out) {
+  } else if (ow >= 0) {
     // ---------------- output waves ------------------------------------------
-    const int ow = wave == 3 ? 0 : 1;
     OutRegs<T, D> r0, r1, r2;
     if (nc == 0) {
       lds_sync();
@@ -657,34 +688,34 @@ state_output_kernel(Args a) {
     r1.issue(a, ch0 + (int64_t)min(1, nc - 1), lane, ow);
     int st = 2;
     for (; st + 3 <= nc + 2; st += 3) {
-      output_wave_step<T, D>(a, st, nc, len, sbos, ch0, jg, h, lane, ow, r2, r0, xbuf);
-      output_wave_step<T, D>(a, st + 1, nc, len, sbos, ch0, jg, h, lane, ow, r0, r1, xbuf);
-      output_wave_step<T, D>(a, st + 2, nc, len, sbos, ch0, jg, h, lane, ow, r1, r2, xbuf);
+      output_wave_step<T, D, TW>(a, st, nc, len, sbos, ch0, jg0, h, lane, ow, r2, r0, xbuf);
+      output_wave_step<T, D, TW>(a, st + 1, nc, len, sbos, ch0, jg0, h, lane, ow, r0, r1, xbuf);
+      output_wave_step<T, D, TW>(a, st + 2, nc, len, sbos, ch0, jg0, h, lane, ow, r1, r2, xbuf);
     }
     if (st < nc + 2) {
-      output_wave_step<T, D>(a, st, nc, len, sbos, ch0, jg, h, lane, ow, r2, r0, xbuf);
+      output_wave_step<T, D, TW>(a, st, nc, len, sbos, ch0, jg0, h, lane, ow, r2, r0, xbuf);
       ++st;
     }
-    if (st < nc + 2) output_wave_step<T, D>(a, st, nc, len, sbos, ch0, jg, h, lane, ow, r0, r1, xbuf);
-  } else if (wave == kWarmWave) {
+    if (st < nc + 2) output_wave_step<T, D, TW>(a, st, nc, len, sbos, ch0, jg0, h, lane, ow, r0, r1, xbuf);
+  } else if (wave == R::kWarm) {
     // ---------------- L2 warm-up wave ---------------------------------------
     const int ahead = a.warm;
-    for (int cc = 0; cc < ahead && cc < nc; ++cc) L2Warm<T, D>::touch(a, ch0 + cc, jg, lane, junk);
+    for (int cc = 0; cc < ahead && cc < nc; ++cc) L2Warm<T, D, TW>::touch(a, ch0 + cc, jw, lane, junk);
     for (int st = 0; st <= nc + 1; ++st) {
       __builtin_amdgcn_s_barrier();
-      if (ahead > 0 && st + ahead < nc) L2Warm<T, D>::touch(a, ch0 + (int64_t)(st + ahead), jg, lane, junk);
+      if (ahead > 0 && st + ahead < nc) L2Warm<T, D, TW>::touch(a, ch0 + (int64_t)(st + ahead), jw, lane, junk);
     }
     wait_vm<0>();
-  } else {
+  } else if (part >= 0) {
     // ---------------- loader waves ------------------------------------------
-    const LD ld{(int64_t)jg * (SG::U_TILE_BYTES / 16), lane, wave - 1};
+    const LD ld{(int64_t)jg0 * (SG::U_TILE_BYTES / 16), lane, part};
     for (int cc = 0; cc < AHEAD && cc < nc; ++cc) ld.issue(a, ch0 + (int64_t)cc, cslots[cc]);
     for (int st = 0; st <= nc + 1; ++st) {
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       if (st + AHEAD < nc) ld.issue(a, ch0 + (int64_t)(st + AHEAD), cslots[(st + AHEAD) % NSLOT]);
       // chunk st must have landed before the next barrier; the loads issued
-      // after it (chunks st + 1, st + 2 where they exist) may stay in flight
+      // after it (up to AHEAD newer chunks where they exist) may stay in flight
       if (st < nc) {
         const int newer = min(AHEAD, nc - 1 - st);
         if (newer >= 2) wait_vm<2 * LD::MIN_PER_PART>();
@@ -692,7 +723,19 @@ state_output_kernel(Args a) {
         else wait_vm<0>();
       }
     }
+  } else {
+    // ---------------- barrier-only wave -------------------------------------
+    for (int st = 0; st <= nc + 1; ++st) __builtin_amdgcn_s_barrier();
   }
+}
+
+template <typename T, int D, int TW>
+static hipError_t launch_state_output_tw(const Args &a, hipStream_t s) {
+  constexpr int NWG = D / 16 / TW;
+  const int64_t units = (int64_t)a.N * a.H;
+  const int64_t blocks = ((units + 7) / 8) * 8 * NWG;
+  state_output_kernel<T, D, TW><<<dim3((unsigned)blocks), dim3(64 * FusedRoles<TW>::kWaves), 0, s>>>(a);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -700,10 +743,12 @@ static hipError_t launch_state_output_t(const Args &a, hipStream_t s) {
   constexpr int NT = D / 16;
   const int64_t units = (int64_t)a.N * a.H;
   if (units == 0) return hipSuccess;
-  const int64_t blocks = ((units + 7) / 8) * 8 * NT;
-  state_output_kernel<T, D>
-      <<<dim3((unsigned)blocks), dim3(64 * (1 + kFusedOutWaves + kFusedLoadWaves + kFusedWarmWaves)), 0, s>>>(a);
-  return hipGetLastError();
+  // one workgroup per CU (LDS): two tiles per workgroup once the one-tile
+  // grid no longer fits on the CUs at once (the GVA batch with 32 heads and 8
+  // sequences: 0.427 -> 0.317 ms); up to that the chain bounds the pass and
+  // one tile per workgroup spreads it over more CUs
+  if (units * NT > (int64_t)(a.num_cus > 0 ? a.num_cus : 1)) return launch_state_output_tw<T, D, 2>(a, s);
+  return launch_state_output_tw<T, D, 1>(a, s);
 }
 
 hipError_t launch_state_output(const Args &a, hipStream_t s) {
