@@ -633,8 +633,8 @@ state_output_kernel(Args a) {
   const int u = (b / (8 * NWG)) * 8 + (b & 7);
   const int H = a.H;
   if (u >= a.N * H) return;
-  const int seq = u / H, h = u % H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int seq = seq_by_length(a, u / H, lane), h = u % H;
   const int g = lane >> 4, c = lane & 15;
 
   int f0, nc, len, sbos;
