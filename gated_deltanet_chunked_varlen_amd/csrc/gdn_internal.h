@@ -142,29 +142,44 @@ __device__ __forceinline__ void seq_geometry(const Args &a, int seq, int lane, i
   }
 }
 
-// The sequence of rank r when sequences are ordered by decreasing chunk
-// count (ties by index), for the calling wave.  Workgroups taken in this
-// order start the longest chains first, so a batch of uneven lengths that
-// needs several rounds of workgroups does not end on a tail of its longest
-// chains.  Direct mode only (the lanes hold the geometry); with the chunk
-// table the batch order stays.
-__device__ __forceinline__ int seq_by_length(const Args &a, int r, int lane) {
-  if (!a.direct) return r;
-  const SeqLane s = seq_lane(a.cu, a.cu_type, a.N, a.T, lane);
-  const int n = lane < a.N ? s.cc1 - s.cc0 : -1;
-  int rank = 0;
-  for (int j = 0; j < a.N; ++j) {
-    const int nj = __shfl(n, j);
-    rank += (nj > n || (nj == n && j < lane)) ? 1 : 0;
-  }
-  const unsigned long long m = __ballot(lane < a.N && rank == r);
-  return m ? __ffsll((long long)m) - 1 : r;
-}
-
 __device__ __forceinline__ void seq_geometry(const Args &a, int seq, int lane, int &f0, int &nc,
                                              int &len) {
   int bos;
   seq_geometry(a, seq, lane, f0, nc, len, bos);
+}
+
+// The sequence of rank r when sequences are ordered by decreasing chunk
+// count (ties by index), from the lanes' geometry s of a direct-mode batch.
+// Workgroups taken in this order start the longest chains first, so a batch
+// of uneven lengths that needs several rounds of workgroups does not end on
+// a tail of its longest chains.
+__device__ __forceinline__ int seq_by_length(const SeqLane &s, int N, int r, int lane) {
+  const int n = lane < N ? s.cc1 - s.cc0 : -1;
+  int rank = 0;
+  for (int j = 0; j < N; ++j) {
+    const int nj = __shfl(n, j);
+    rank += (nj > n || (nj == n && j < lane)) ? 1 : 0;
+  }
+  const unsigned long long m = __ballot(lane < N && rank == r);
+  return m ? __ffsll((long long)m) - 1 : r;
+}
+
+// seq_geometry for the workgroup of unit rank r, longest sequences first in
+// direct mode (cu_seqlens read once for both); batch order with the chunk
+// table.
+__device__ __forceinline__ int seq_geometry_by_length(const Args &a, int r, int lane, int &f0,
+                                                      int &nc, int &len, int &bos) {
+  if (a.direct) {
+    const SeqLane s = seq_lane(a.cu, a.cu_type, a.N, a.T, lane);
+    const int seq = seq_by_length(s, a.N, r, lane);
+    f0 = __shfl(s.cc0, seq);
+    nc = __shfl(s.cc1, seq) - f0;
+    len = __shfl(s.len, seq);
+    bos = __shfl(s.bos, seq);
+    return seq;
+  }
+  seq_geometry(a, r, lane, f0, nc, len, bos);
+  return r;
 }
 #endif
 

@@ -634,11 +634,11 @@ state_output_kernel(Args a) {
   const int H = a.H;
   if (u >= a.N * H) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int seq = seq_by_length(a, u / H, lane), h = u % H;
+  const int h = u % H;
   const int g = lane >> 4, c = lane & 15;
 
   int f0, nc, len, sbos;
-  seq_geometry(a, seq, lane, f0, nc, len, sbos);
+  const int seq = seq_geometry_by_length(a, u / H, lane, f0, nc, len, sbos);
   const int64_t ch0 = ws_index(f0, h, a.cap);
 
   const int ct = R::compute_tile(wave), ow = R::out_index(wave), part = R::loader_part(wave);
