@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/gdn_prefill.h"
 #include "gdn_common.h"
 
@@ -12,6 +14,21 @@ namespace gdn {
 // Largest batch whose sequence geometry one wave64 holds (lane i = sequence i,
 // lane N = the end offset).
 constexpr int kDirectSeqs = 63;
+
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per device (the attribute belongs to the device current when it is set);
+// `done` holds one bit per device id below 64.  Threads that race both set
+// it, which is harmless.
+inline hipError_t set_dynamic_lds(const void *fn, int bytes, std::atomic<uint64_t> &done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 // Everything a kernel may read, passed by value.  Pointers are device
 // pointers; strides are in elements.

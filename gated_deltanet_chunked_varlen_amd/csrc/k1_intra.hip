@@ -274,12 +274,10 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
 template <typename T, int D>
 static hipError_t launch_intra_t(const Args &a, hipStream_t s) {
   const size_t smem = sizeof(IntraSmem<T, D>);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)intra_kernel<T, D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = set_dynamic_lds((const void *)intra_kernel<T, D>, (int)smem, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int64_t blocks = a.cap * a.H;
   if (blocks == 0) return hipSuccess;
@@ -599,12 +597,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
 template <typename T, int D, bool NTS>
 static hipError_t launch_intra_h_nt(const Args &a, hipStream_t s) {
   const size_t smem = sizeof(IntraSmemB<T, D>);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)intra_kernel_h<T, D, NTS>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = set_dynamic_lds((const void *)intra_kernel_h<T, D, NTS>, (int)smem, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int64_t blocks = a.cap * a.H;
   if (blocks == 0) return hipSuccess;

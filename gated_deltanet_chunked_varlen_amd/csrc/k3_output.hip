@@ -179,12 +179,10 @@ __global__ void __launch_bounds__(256) output_kernel(Args a) {
 template <typename T, int D>
 static hipError_t launch_output_t(const Args &a, hipStream_t s) {
   const size_t smem = sizeof(OutSmem<T, D>);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)output_kernel<T, D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = set_dynamic_lds((const void *)output_kernel<T, D>, (int)smem, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int64_t blocks = a.cap * a.H;
   if (blocks == 0) return hipSuccess;
