@@ -297,6 +297,39 @@ def test_many_sequences_chunk_table_path():
     _check(wl, gpu, tl.run_oracle(wl))
 
 
+# Batches whose one-tile state-pass grid outgrows the CUs take two 16-column
+# tiles per workgroup and start the longest sequences first.  Configs 3 and 4
+# and the chunk-table case above reach that only at D = 128 or through the
+# table; these reach it in the direct (up to 63 sequences) geometry at every
+# head size, with uneven lengths, an empty sequence, pools and checkpoints.
+TWO_TILE_CASES = {
+    "d64_f16_pool": dict(heads=(12, 12, 12), D=64, dtype="f16", l2norm_in_kernel=True,
+                         init="pool", pool_size=48, in_place_pool=True, init_dtype="f16",
+                         final_state_dtype="f16", checkpoint_every=128),
+    "d32_bf16_gqa": dict(heads=(16, 4, 4), D=32, dtype="bf16", normalise_in_generator=True,
+                         init="seq", init_dtype="bf16", checkpoint_every=64),
+    "d128_bf16_gva_e4m3": dict(heads=(4, 4, 8), D=128, dtype="bf16", l2norm_in_kernel=True,
+                               init="pool", pool_size=41, in_place_pool=True,
+                               init_dtype="e4m3", final_state_dtype="e4m3"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(TWO_TILE_CASES))
+def test_two_tile_workgroups(case):
+    kw = dict(TWO_TILE_CASES[case])
+    hq, hk, hv = kw.pop("heads")
+    D, dtype = kw.pop("D"), kw.pop("dtype")
+    seed = 40 + sorted(TWO_TILE_CASES).index(case)
+    rng = np.random.default_rng(seed)
+    lengths = [int(x) for x in rng.integers(1, 400, size=40)]
+    lengths[7] = 0
+    wl = W.make(seed, lengths, hq, hk, hv, D, dtype, name="two_tile_" + case, **kw)
+    assert wl.N * wl.H * (D // 16) > 256, "the case must outgrow one round of workgroups"
+    gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] == 0
+    _check(wl, gpu, tl.run_oracle(wl))
+
+
 @pytest.mark.parametrize("nseq", [3, 80])
 def test_status_bad_cu_seqlens_full_call(nseq):
     # a decreasing offset is flagged on both geometry paths (up to 63
