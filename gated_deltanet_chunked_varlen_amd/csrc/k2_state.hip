@@ -583,7 +583,7 @@ __device__ __forceinline__ void output_wave_step(const Args &a, int st, int nc, 
                       min(kChunk, len - kChunk * oc), h, lane, ow);
 }
 
-constexpr int kFusedOutWaves = 2, kFusedLoadWaves = 2;
+constexpr int kFusedLoadWaves = 2;
 
 // Waves of the fused pass: TW = 1 as in the header comment (six waves); TW = 2
 // (eight): compute waves 0 and 2 (one per column tile), output waves 1 and 3
