@@ -449,6 +449,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="calls timed after flushing the last-level cache (0: none)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -562,6 +564,28 @@ def main():
         L.hipEventDestroy(a)
         L.hipEventDestroy(b)
 
+    # cold last-level cache, beside the warm steady state above: before each
+    # of a few calls, 512 MiB (twice the 256 MB last-level cache) are written
+    # on the call's stream, and the call alone is timed between the first and
+    # last of its phase events
+    cold = None
+    if args.cold_calls > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ce = [(new_event(L), new_event(L)) for _ in range(args.cold_calls)]
+        for i in range(args.cold_calls):
+            flush.fill_(i & 0xFF)
+            e5 = (ctypes.c_void_p * 5)()
+            e5[0], e5[4] = ce[i][0], ce[i][1]
+            call(e5)
+        torch.cuda.synchronize()
+        cms = float(np.median([elapsed_ms(L, a, b) for a, b in ce]))
+        for a, b in ce:
+            L.hipEventDestroy(a)
+            L.hipEventDestroy(b)
+        del flush
+        cold = {"ms_per_call_median": cms, "tokens_per_s": T / (cms / 1e3),
+                "flush_bytes": 512 << 20, "calls": args.cold_calls}
+
     ms_step = ms_total / K
     tokens_per_s = T * K / (ms_total / 1e3)
     flops = T * H * FLOPS_PER_TOKEN_HEAD(D)
@@ -600,6 +624,7 @@ def main():
                      "timing": "HIP events around the kernel in each of K further steps",
                      "algorithmic_bytes_per_launch": bytes_launch},
         "wall_s_timed": wall,
+        "cold_cache": cold,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
