@@ -323,8 +323,8 @@ def summarize_mfma(argv):
     lines = ["# Matrix-core counters: %s" % wname, "",
              "Command:", "", "    " + cmd, "",
              "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
-             "executed matrix FLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (fp16 inputs count "
-             "under F16 and read 0 here). Counter runs serialise and lengthen kernels, so the "
+             "executed matrix FLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (fp16 and fp32 inputs "
+             "count under F16 / F32 and read 0 here). Counter runs serialise and lengthen kernels, so the "
              "busy fraction is a lower bound on the unprofiled one.", "",
              "| kernel | dispatches | MFMA busy | executed matrix GFLOP per launch |",
              "|---|---|---|---|"]
