@@ -330,6 +330,34 @@ def test_two_tile_workgroups(case):
     _check(wl, gpu, tl.run_oracle(wl))
 
 
+def test_sequence_results_do_not_depend_on_batch_position():
+    # Every (sequence, head, tile) is computed on its own: taking the batch in
+    # another order (here reversed, 40 uneven sequences, so the state pass
+    # takes two tiles per workgroup and starts the longest sequences first)
+    # must give each sequence bit-identical outputs and final states.
+    import copy
+    rng = np.random.default_rng(45)
+    lengths = [int(x) for x in rng.integers(1, 400, size=40)]
+    lengths[11] = 0
+    a = W.make(45, lengths, 8, 8, 8, 128, "bf16", l2norm_in_kernel=True, init="seq",
+               name="order_a")
+    assert a.N * a.H * 8 > 256
+    cu = a.cu_seqlens.astype(np.int64)
+    order = list(range(a.N))[::-1]
+    rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in order]).astype(np.int64)
+    b = copy.deepcopy(a)
+    b.q, b.k, b.v = a.q[rows], a.k[rows], a.v[rows]
+    b.g, b.beta = a.g[rows], a.beta[rows]
+    b.initial_state = a.initial_state[order]
+    nl = [lengths[i] for i in order]
+    b.cu_seqlens = np.concatenate([[0], np.cumsum(nl)]).astype(a.cu_seqlens.dtype)
+    ra, rb = tl.run_gpu(a), tl.run_gpu(b)
+    cub = b.cu_seqlens.astype(np.int64)
+    for pos, i in enumerate(order):
+        assert np.array_equal(ra["out"][cu[i]:cu[i + 1]], rb["out"][cub[pos]:cub[pos + 1]]), i
+        assert np.array_equal(ra["final"][i], rb["final"][pos]), i
+
+
 @pytest.mark.parametrize("nseq", [3, 80])
 def test_status_bad_cu_seqlens_full_call(nseq):
     # a decreasing offset is flagged on both geometry paths (up to 63
