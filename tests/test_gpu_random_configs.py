@@ -28,9 +28,11 @@ def _gpu():
 HEADS = [(2, 2, 2), (4, 2, 2), (2, 2, 4), (3, 3, 3), (1, 1, 4), (4, 1, 1)]
 
 
-def _case(seed):
+def _case(seed, many=False):
     rng = np.random.default_rng(7000 + seed)
-    n = int(rng.integers(1, 8))
+    # many: batches of 33-50 sequences, which with the larger head counts and
+    # sizes take the state pass's two-tile workgroups and longest-first order
+    n = int(rng.integers(33, 51)) if many else int(rng.integers(1, 8))
     lengths = [int(x) for x in rng.integers(0, 301, size=n)]
     if rng.random() < 0.3:
         lengths[int(rng.integers(0, n))] = 0
@@ -55,13 +57,15 @@ def _case(seed):
                   checkpoint_dtype=str(rng.choice(["f32", "bf16", "e4m3"])))
     if not kw["l2norm_in_kernel"]:
         kw["normalise_in_generator"] = True
-    wl = W.make(8000 + seed, lengths, hq, hk, hv, D, dtype, name="random%d" % seed, **kw)
+    wl = W.make(8000 + seed, lengths, hq, hk, hv, D, dtype,
+                name=("random_many%d" if many else "random%d") % seed, **kw)
     return wl
 
 
-@pytest.mark.parametrize("seed", range(16))
-def test_random_config(seed):
-    wl = _case(seed)
+@pytest.mark.parametrize("seed,many", [(s, False) for s in range(16)] +
+                         [(s, True) for s in range(100, 108)])
+def test_random_config(seed, many):
+    wl = _case(seed, many)
     gpu = tl.run_gpu(wl, status=True)
     assert gpu["status"] == 0
     orc = tl.run_oracle(wl)
