@@ -590,6 +590,17 @@ def main():
 
     ms_step = ms_total / K
     tokens_per_s = T * K / (ms_total / 1e3)
+    # the whole call: counter-measured HBM bytes of every kernel it launches
+    # (where the committed counters match the kernel sources) over the
+    # measured time per step
+    per_phase = {ph: load_traffic(ph, wl.name) for ph in PHASES if phase_ms[ph] > 0.0}
+    known = {ph: b for ph, b in per_phase.items() if b is not None}
+    call_traffic = None
+    if known and set(known) >= {"intra", "state"}:
+        tb = sum(known.values())
+        gbs = tb / (ms_step / 1e3) / 1e9
+        call_traffic = {"bytes": tb, "phases": sorted(known), "achieved": gbs,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
     flops = T * H * FLOPS_PER_TOKEN_HEAD(D)
     tflops = flops / (ms_step / 1e3) / 1e12
     peak_mm = FP32_PEAK_TFLOPS if wl.dtype == "f32" else BF16_PEAK_TFLOPS   # fp16 peak = bf16 peak
@@ -627,6 +638,7 @@ def main():
                      "algorithmic_bytes_per_launch": bytes_launch},
         "wall_s_timed": wall,
         "cold_cache": cold,
+        "call_traffic": call_traffic,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
