@@ -587,10 +587,12 @@ constexpr int kFusedLoadWaves = 2;
 
 // Waves of the fused pass: TW = 1 as in the header comment (six waves); TW = 2
 // (eight): compute waves 0 and 2 (one per column tile), output waves 1 and 3
-// (each for both tiles), L2 warm-up wave 4, loaders 5 and 7, and wave 6 only
+// (each for both tiles), loaders 4 and 6, L2 warm-up wave 5, and wave 7 only
 // keeps the step barriers.  Waves are dealt to the CU's four SIMDs in turn
 // (wave w on SIMD w % 4), so each SIMD holds one matrix-core-heavy wave and
-// one light one.
+// one light one.  With two tiles the loaders bound the step and the compute
+// waves wait at its barrier, so the loaders share the compute waves' SIMDs,
+// not the busier output waves'.
 template <int TW> struct FusedRoles;
 template <> struct FusedRoles<1> {
   static constexpr int kWaves = 6, kSlots = 4, kWarm = 4;
@@ -599,10 +601,10 @@ template <> struct FusedRoles<1> {
   __device__ static int loader_part(int w) { return w == 1 ? 0 : w == 2 ? 1 : -1; }
 };
 template <> struct FusedRoles<2> {
-  static constexpr int kWaves = 8, kSlots = 3, kWarm = 4;
+  static constexpr int kWaves = 8, kSlots = 3, kWarm = 5;
   __device__ static int compute_tile(int w) { return w == 0 ? 0 : w == 2 ? 1 : -1; }
   __device__ static int out_index(int w) { return w == 1 ? 0 : w == 3 ? 1 : -1; }
-  __device__ static int loader_part(int w) { return w == 5 ? 0 : w == 7 ? 1 : -1; }
+  __device__ static int loader_part(int w) { return w == 4 ? 0 : w == 6 ? 1 : -1; }
 };
 
 // TW column tiles per workgroup.  TW = 2 shares the workgroup's W / Ktilde
