@@ -349,6 +349,7 @@ __global__ void __launch_bounds__(64) state_kernel(Args a) {
 //               and the gate row into a four-slot ring, two chunks ahead;
 //   wave 4      L2 warm-up (when the intermediates live in HBM): touches
 //               the lines of the chunk two ahead.
+// When the intermediates live in HBM, waves 1 and 4 swap roles (below).
 // Step st (one barrier each): the loaders start chunk st + 2 and wait for
 // chunk st, the compute wave works on chunk st - 1, the output waves on
 // chunk st - 2 and start fetching chunk st.
@@ -590,21 +591,27 @@ constexpr int kFusedLoadWaves = 2;
 // (each for both tiles), loaders 4 and 6, L2 warm-up wave 5, and wave 7 only
 // keeps the step barriers.  Waves are dealt to the CU's four SIMDs in turn
 // (wave w on SIMD w % 4), so each SIMD holds one matrix-core-heavy wave and
-// one light one.  With two tiles the loaders bound the step and the compute
-// waves wait at its barrier, so the loaders share the compute waves' SIMDs,
-// not the busier output waves'.
+// one light one.  A loader shares the compute wave's SIMD where the loaders,
+// not the compute wave, bound the step (the compute wave then waits at the
+// step barrier): always with two tiles, and with one tile when the
+// intermediates live in HBM (hbm: the L2 warm-up is on), where loader 0
+// moves from wave 1 to wave 4 and the warm-up wave to wave 1.
 template <int TW> struct FusedRoles;
 template <> struct FusedRoles<1> {
-  static constexpr int kWaves = 6, kSlots = 4, kWarm = 4;
+  static constexpr int kWaves = 6, kSlots = 4;
   __device__ static int compute_tile(int w) { return w == 0 ? 0 : -1; }
   __device__ static int out_index(int w) { return w == 3 ? 0 : w == 5 ? 1 : -1; }
-  __device__ static int loader_part(int w) { return w == 1 ? 0 : w == 2 ? 1 : -1; }
+  __device__ static int warm_wave(bool hbm) { return hbm ? 1 : 4; }
+  __device__ static int loader_part(int w, bool hbm) {
+    return w == (hbm ? 4 : 1) ? 0 : w == 2 ? 1 : -1;
+  }
 };
 template <> struct FusedRoles<2> {
-  static constexpr int kWaves = 8, kSlots = 3, kWarm = 5;
+  static constexpr int kWaves = 8, kSlots = 3;
   __device__ static int compute_tile(int w) { return w == 0 ? 0 : w == 2 ? 1 : -1; }
   __device__ static int out_index(int w) { return w == 1 ? 0 : w == 3 ? 1 : -1; }
-  __device__ static int loader_part(int w) { return w == 4 ? 0 : w == 6 ? 1 : -1; }
+  __device__ static int warm_wave(bool) { return 5; }
+  __device__ static int loader_part(int w, bool) { return w == 4 ? 0 : w == 6 ? 1 : -1; }
 };
 
 // TW column tiles per workgroup.  TW = 2 shares the workgroup's W / Ktilde
@@ -643,7 +650,8 @@ state_output_kernel(Args a) {
   const int seq = seq_geometry_by_length(a, u / H, lane, f0, nc, len, sbos);
   const int64_t ch0 = ws_index(f0, h, a.cap);
 
-  const int ct = R::compute_tile(wave), ow = R::out_index(wave), part = R::loader_part(wave);
+  const bool hbm = a.warm > 0;
+  const int ct = R::compute_tile(wave), ow = R::out_index(wave), part = R::loader_part(wave, hbm);
   if (ct >= 0) {
     // ---------------- compute wave (column tile jg0 + ct) --------------------
     const int jg = jg0 + ct;
@@ -699,7 +707,7 @@ state_output_kernel(Args a) {
       ++st;
     }
     if (st < nc + 2) output_wave_step<T, D, TW>(a, st, nc, len, sbos, ch0, jg0, h, lane, ow, r0, r1, xbuf);
-  } else if (wave == R::kWarm) {
+  } else if (wave == R::warm_wave(hbm)) {
     // ---------------- L2 warm-up wave ---------------------------------------
     const int ahead = a.warm;
     for (int cc = 0; cc < ahead && cc < nc; ++cc) L2Warm<T, D, TW>::touch(a, ch0 + cc, jw, lane, junk);
