@@ -15,7 +15,7 @@ dominant kernel (timed live with HIP events recorded around it on the call's
 stream, in K further steps) and the CPU oracle's throughput on the same
 workload (a bounded number of repetitions on this host's cores).
 
-    python bench.py [--steps K] [--warmup W] [--workload c2]
+    python bench.py [--steps K] [--warmup W] [--workload varlen2x2048]
     python bench.py --workload decode       # the decode step, its own line
     python bench.py --copy-calibration      # plain 1 GiB copies, for counters
     python bench.py --summarize <workload> <rocprofv3 output dirs...> <command>
@@ -443,9 +443,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--workload", default="c2",
-                    help="c2 (default, the headline); c1..c5 for analysis; "
-                         "decode for the decode step (its own JSON line)")
+    ap.add_argument("--workload", default="varlen2x2048",
+                    help="varlen2x2048 (default, the headline); single128, "
+                         "ragged6, gva8, long262144 for analysis; decode for "
+                         "the decode step (its own JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")

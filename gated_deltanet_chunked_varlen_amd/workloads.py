@@ -231,7 +231,7 @@ def make(seed: int, lengths, hq: int, hk: int, hv: int, D: int,
 
 # The five named workloads, seeds 1000 + index.
 
-def c1_single_small() -> Workload:
+def single_l128_h1_d32_f32() -> Workload:
     """1 sequence of 128 tokens (2 chunks), 1 head, head size 32, fp32,
     q/k unit rows from the generator, alpha ~ U[0.9, 1], beta = sigmoid(N(0,1)),
     scale 1/sqrt(32), zero initial state."""
@@ -239,14 +239,14 @@ def c1_single_small() -> Workload:
                 scale=1.0 / np.sqrt(32.0), name="single_L128_h1_d32_f32")
 
 
-def c2_two_by_2048() -> Workload:
+def varlen_2x2048_h16_d128() -> Workload:
     """2 x 2048 tokens, 16 heads, head size 128, bf16, in-kernel q/k L2
     norm, alpha ~ U[0.9, 1], zero initial state, fp32 final state."""
     return make(1001, [2048, 2048], 16, 16, 16, 128, "bf16",
                 l2norm_in_kernel=True, name="varlen_2x2048_h16_d128_bf16")
 
 
-def c3_ragged_pool() -> Workload:
+def ragged6_pool64_h16_d128() -> Workload:
     """Lengths [130, 20, 300, 0, 64, 1], 16 heads, head size 128, bf16,
     in-kernel q/k L2 norm, fp32 64-slot pool ~ N(0, 0.02) read and written in
     place through unique state_indices."""
@@ -255,7 +255,7 @@ def c3_ragged_pool() -> Workload:
                 in_place_pool=True, name="ragged6_pool64_h16_d128_bf16")
 
 
-def c4_gva_checkpoints() -> Workload:
+def gva8_h16x32_d128_checkpoints() -> Workload:
     """8 sequences with lengths ~ U[1, 8192], 16 q/k heads and 32 v heads,
     head size 128, bf16, alpha ~ U[0.85, 1], in-kernel q/k L2 norm,
     checkpoints every 1024 tokens, fp32 final states."""
@@ -265,7 +265,7 @@ def c4_gva_checkpoints() -> Workload:
                 name="gva8_h16x32_d128_bf16_ckpt1024")
 
 
-def c5_long_single() -> Workload:
+def long_l262144_h32_d128() -> Workload:
     """One sequence of 262144 tokens (4096 chunks), 32 heads, head size 128,
     bf16, q/k unit rows from the generator, alpha ~ U[0.95, 1], bf16 initial
     state ~ N(0, 0.02), fp32 final state."""
@@ -286,10 +286,10 @@ def decode_batch() -> Workload:
 
 
 WORKLOADS = {
-    "c1": c1_single_small,
-    "c2": c2_two_by_2048,
-    "c3": c3_ragged_pool,
-    "c4": c4_gva_checkpoints,
-    "c5": c5_long_single,
+    "single128": single_l128_h1_d32_f32,
+    "varlen2x2048": varlen_2x2048_h16_d128,
+    "ragged6": ragged6_pool64_h16_d128,
+    "gva8": gva8_h16x32_d128_checkpoints,
+    "long262144": long_l262144_h32_d128,
     "decode": decode_batch,
 }

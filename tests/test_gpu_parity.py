@@ -84,8 +84,8 @@ def test_chunk_index_flags_bad_cu_seqlens():
 
 # ------------------------------------------------------------- named configs
 
-def test_c1_single_small_fp32():
-    wl = W.c1_single_small()
+def test_single_l128_h1_d32_f32_fp32():
+    wl = W.single_l128_h1_d32_f32()
     gpu = tl.run_gpu(wl)
     orc = tl.run_oracle(wl)
     _check(wl, gpu, orc)
@@ -94,13 +94,13 @@ def test_c1_single_small_fp32():
     np.testing.assert_allclose(gpu["final"], orc["final"], rtol=1e-4, atol=1e-5)
 
 
-def test_c2_two_by_2048():
-    wl = W.c2_two_by_2048()
+def test_varlen_2x2048_h16_d128():
+    wl = W.varlen_2x2048_h16_d128()
     _check(wl, tl.run_gpu(wl), tl.run_oracle(wl))
 
 
-def test_c3_ragged_pool_in_place():
-    wl = W.c3_ragged_pool()
+def test_ragged6_pool64_h16_d128_in_place():
+    wl = W.ragged6_pool64_h16_d128()
     gpu = tl.run_gpu(wl, status=True)
     orc = tl.run_oracle(wl)
     assert gpu["status"] == 0
@@ -225,7 +225,7 @@ def test_checkpoints_every_64_and_bf16_checkpoint_rows():
 
 
 def test_determinism_bitwise():
-    wl = W.c3_ragged_pool()
+    wl = W.ragged6_pool64_h16_d128()
     a = tl.run_gpu(wl)
     b = tl.run_gpu(wl)
     np.testing.assert_array_equal(a["out"], b["out"])
@@ -394,8 +394,8 @@ def test_host_errors_raise_before_launch():
 
 # ------------------------------------------------- large named configs (last)
 
-def test_c4_gva_checkpoints():
-    wl = W.c4_gva_checkpoints()
+def test_gva8_h16x32_d128_checkpoints():
+    wl = W.gva8_h16x32_d128_checkpoints()
     heads = [0, 1, 17, 31]
     gpu = tl.run_gpu(wl, status=True)
     assert gpu["status"] == 0
@@ -428,8 +428,8 @@ def test_large_call_form_d32_bf16_gqa():
 
 
 @pytest.mark.timeout(600)
-def test_c5_long_single_sampled_heads():
-    wl = W.c5_long_single()
+def test_long_l262144_h32_d128_sampled_heads():
+    wl = W.long_l262144_h32_d128()
     heads = [0, 31]
     gpu = tl.run_gpu(wl)
     orc = tl.run_oracle(wl, heads=heads)
