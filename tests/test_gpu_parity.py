@@ -297,6 +297,24 @@ def test_many_sequences_chunk_table_path():
     _check(wl, gpu, tl.run_oracle(wl))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_more_sequences_than_one_scan_block(dtype):
+    # 1500 sequences: the chunk-index builder's scan takes several passes of
+    # its block, inside a whole call, with a pool of 1600 rows in place
+    rng = np.random.default_rng(33)
+    lengths = [int(x) for x in rng.integers(0, 90, size=1500)]
+    for i in rng.choice(1500, 200, replace=False):
+        lengths[int(i)] = 0
+    wl = _small(33, lengths, dtype=dtype, D=32, init="pool", pool_size=1600,
+                in_place_pool=True, checkpoint_every=64)
+    gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] == 0
+    _check(wl, gpu, tl.run_oracle(wl))
+    rows = set(int(r) for r in wl.state_indices)
+    others = [r for r in range(1600) if r not in rows]
+    np.testing.assert_array_equal(gpu["final"][others], gpu["pool_before"][others])
+
+
 # Batches whose one-tile state-pass grid outgrows the CUs take two 16-column
 # tiles per workgroup and start the longest sequences first.  Configs 3 and 4
 # and the chunk-table case above reach that only at D = 128 or through the
