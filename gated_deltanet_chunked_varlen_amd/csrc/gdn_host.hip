@@ -252,7 +252,11 @@ int gdn_build_chunk_indices(const void *cu_seqlens, int32_t cu_type, int32_t num
 // Above this many bytes of intermediates the fused pass finds them in HBM
 // rather than in the 256 MB last-level cache (the intra-chunk pass streams
 // q, k and v through it as well), and warming L2 ahead of the loads pays.
-constexpr int64_t kWarmBytes = 128ll << 20;
+// Measured at 16 heads, D = 128 (intermediates over the chunk-count bound):
+// plain stores and no warm-up are faster at 139 and 199 MB (7 and 10
+// sequences of 1024 tokens), the large-call form at 229 and 260 MB (3 x 4096
+// and 13 x 1024 tokens).
+constexpr int64_t kWarmBytes = 200ll << 20;
 
 static void fill_args(const gdn_prefill_params *p, const Layout *L, int num_cus, Args &a) {
   unsigned char *ws = (unsigned char *)p->workspace;

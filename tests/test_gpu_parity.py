@@ -421,16 +421,27 @@ def test_gva8_h16x32_d128_checkpoints():
     _check(wl, gpu, orc, heads=heads)
 
 
-# Calls whose intermediates outgrow the 256 MB last-level cache take the
-# large-call form: non-temporal intermediate stores and the L2 warm-up wave of
-# the state pass.  The configs above reach it only at D = 128; these two reach
-# it at D = 64 (fp16, in-kernel norm, in-place pool, checkpoints) and at D = 32
+# Calls whose intermediates outgrow the last-level cache (above 200 MiB,
+# counted over the chunk-count bound the workspace uses) take the large-call
+# form: non-temporal intermediate stores and the L2 warm-up wave of the state
+# pass.  The configs above reach it only at D = 128; these two reach it at
+# D = 64 (fp16, in-kernel norm, in-place pool, checkpoints) and at D = 32
 # (bf16, no norm, GQA), checked on every head.
+LARGE_CALL_BYTES = 200 << 20
+
+
+def _assert_large_call(wl):
+    chunks = (wl.T + 63 * wl.N) // 64
+    inter = chunks * wl.H * (4 * 64 * wl.D + 64 * 64) * 2
+    assert inter > LARGE_CALL_BYTES, inter
+
+
 @pytest.mark.timeout(600)
 def test_large_call_form_d64_f16_pool_checkpoints():
-    wl = W.make(31, [5000, 4000, 4500], 16, 16, 16, 64, "f16", l2norm_in_kernel=True,
+    wl = W.make(31, [8000, 6500, 7200], 16, 16, 16, 64, "f16", l2norm_in_kernel=True,
                 init="pool", pool_size=7, in_place_pool=True, checkpoint_every=1024,
                 name="large_d64_f16")
+    _assert_large_call(wl)
     gpu = tl.run_gpu(wl, status=True)
     assert gpu["status"] == 0
     _check(wl, gpu, tl.run_oracle(wl))
@@ -438,8 +449,9 @@ def test_large_call_form_d64_f16_pool_checkpoints():
 
 @pytest.mark.timeout(600)
 def test_large_call_form_d32_bf16_gqa():
-    wl = W.make(32, [6100, 130, 4990], 32, 8, 8, 32, "bf16", normalise_in_generator=True,
+    wl = W.make(32, [9800, 130, 8000], 32, 8, 8, 32, "bf16", normalise_in_generator=True,
                 init="seq", name="large_d32_bf16")
+    _assert_large_call(wl)
     gpu = tl.run_gpu(wl, status=True)
     assert gpu["status"] == 0
     _check(wl, gpu, tl.run_oracle(wl))
