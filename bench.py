@@ -352,10 +352,9 @@ def bench_decode(args):
     from gated_deltanet_chunked_varlen_amd import workloads as W
     from gated_deltanet_chunked_varlen_amd import api
     from gated_deltanet_chunked_varlen_amd import _native as nat
-    from tests import gdn_testlib as tl
 
     wl = W.WORKLOADS["decode"]()
-    d = tl.to_device(wl)
+    d = W.to_device(wl)
     N, H, D = wl.N, wl.H, wl.D
     pool = d["initial_state"]
     p, out, outst = api.make_params(
@@ -477,10 +476,9 @@ def main():
     from gated_deltanet_chunked_varlen_amd import workloads as W
     from gated_deltanet_chunked_varlen_amd import api
     from gated_deltanet_chunked_varlen_amd import _native as nat
-    from tests import gdn_testlib as tl
 
     wl = W.WORKLOADS[args.workload]()
-    d = tl.to_device(wl)
+    d = W.to_device(wl)
     H, D, N, T = wl.H, wl.D, wl.N, wl.T
     kw = dict(g=d["g"], beta=d["beta"], scale=wl.scale, cu_seqlens=d["cu_seqlens"],
               use_qk_l2norm_in_kernel=wl.l2norm_in_kernel,

@@ -229,6 +229,42 @@ def make(seed: int, lengths, hq: int, hk: int, hv: int, D: int,
                     checkpoint_cu_starts=ccs, checkpoint_dtype=checkpoint_dtype)
 
 
+
+# ---------------------------------------------------------------- to device
+
+def state_torch_dtype(name):
+    """torch dtype of a state dtype name."""
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
+            "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[name]
+
+
+def to_device(wl, device="cuda"):
+    """The workload's inputs as device tensors in their storage dtypes (a
+    copy, nothing computed): q, k, v, g, beta, cu_seqlens, initial_state,
+    state_indices and checkpoint_cu_starts (None where the workload has
+    none)."""
+    import torch
+    qdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[wl.dtype]
+
+    def t(a, dt):
+        if a is None:
+            return None
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dt)
+
+    def idx(a):
+        return None if a is None else torch.from_numpy(a.copy()).to(device)
+
+    return dict(
+        q=t(wl.q, qdt), k=t(wl.k, qdt), v=t(wl.v, qdt),
+        g=t(wl.g, torch.float32), beta=t(wl.beta, torch.float32),
+        cu_seqlens=idx(wl.cu_seqlens),
+        initial_state=t(wl.initial_state, state_torch_dtype(wl.initial_state_dtype)),
+        state_indices=idx(wl.state_indices),
+        checkpoint_cu_starts=idx(wl.checkpoint_cu_starts),
+    )
+
+
 # The five named workloads, seeds 1000 + index.
 
 def single_l128_h1_d32_f32() -> Workload:

@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from gated_deltanet_chunked_varlen_amd import workloads as W
 from oracle import oracle
 
 TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2 / 8}
@@ -23,10 +24,7 @@ TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2 / 8}
 STORE_TOL = {"f32": 0.0, "bf16": 2.0 ** -8, "f16": 2.0 ** -11,
              "e4m3": 2.0 ** -4, "e5m2": 2.0 ** -3}
 
-def state_torch_dtype(name):
-    torch = _torch()
-    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
-            "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[name]
+state_torch_dtype = W.state_torch_dtype
 
 
 def rel_l2(x, ref):
@@ -72,21 +70,7 @@ def _torch():
     return torch
 
 
-def to_device(wl, device="cuda"):
-    torch = _torch()
-    qdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[wl.dtype]
-    t = lambda a, dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dt)
-    dev = dict(
-        q=t(wl.q, qdt), k=t(wl.k, qdt), v=t(wl.v, qdt),
-        g=t(wl.g, torch.float32), beta=t(wl.beta, torch.float32),
-        cu_seqlens=torch.from_numpy(wl.cu_seqlens.copy()).to(device),
-        initial_state=t(wl.initial_state, state_torch_dtype(wl.initial_state_dtype)),
-        state_indices=None if wl.state_indices is None
-        else torch.from_numpy(wl.state_indices.copy()).to(device),
-        checkpoint_cu_starts=None if wl.checkpoint_cu_starts is None
-        else torch.from_numpy(wl.checkpoint_cu_starts.copy()).to(device),
-    )
-    return dev
+to_device = W.to_device
 
 
 def run_gpu(wl, device="cuda", status=False, **over):
