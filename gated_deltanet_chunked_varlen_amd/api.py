@@ -68,6 +68,25 @@ def _state_strides(t: torch.Tensor):
     return tuple(int(s) for s in t.stride())
 
 
+def _broadcast(t: torch.Tensor) -> bool:
+    """True when a dimension of extent > 1 has stride 0 (an expanded view):
+    its elements alias, and the C ABI reads all-zero strides as
+    "contiguous", so such a view must never reach it as is."""
+    return any(n > 1 and st == 0 for n, st in zip(t.shape, t.stride()))
+
+
+def state_tensor(name: str, t: Optional[torch.Tensor], written: bool):
+    """The state tensor to hand to the library.  An expanded view (a stride
+    of 0 on a dimension of extent > 1) is copied to contiguous memory when the
+    library only reads it, and rejected when the library writes it."""
+    if t is None or not _broadcast(t):
+        return t
+    if written:
+        raise ValueError("%s must not be an expanded view (a stride of 0 on a "
+                         "dimension of extent > 1)" % name)
+    return t.contiguous()
+
+
 def make_params(q, k, v, g=None, beta=None, scale=None, initial_state=None,
                 output_final_state=False, cu_seqlens=None,
                 use_qk_l2norm_in_kernel=False, output=None, output_state=None,
@@ -132,6 +151,7 @@ def make_params(q, k, v, g=None, beta=None, scale=None, initial_state=None,
     if initial_state is not None:
         if initial_state.dtype not in _STATE_DTYPES:
             raise ValueError("unsupported initial_state dtype")
+        initial_state = state_tensor("initial_state", initial_state, written=False)
         p.initial_state = _ptr(initial_state)
         p.initial_state_dtype = _STATE_DTYPES[initial_state.dtype]
         p.initial_state_strides = nat._i64x4(*_state_strides(initial_state))
@@ -152,6 +172,7 @@ def make_params(q, k, v, g=None, beta=None, scale=None, initial_state=None,
             output_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
         if output_state.dtype not in _STATE_DTYPES:
             raise ValueError("unsupported output_state dtype")
+        output_state = state_tensor("output_state", output_state, written=True)
         p.output_final_state = 1
         p.output_state = _ptr(output_state)
         p.output_state_dtype = _STATE_DTYPES[output_state.dtype]
@@ -163,6 +184,7 @@ def make_params(q, k, v, g=None, beta=None, scale=None, initial_state=None,
             if tuple(t.shape) != (rows, H, D, D):
                 raise ValueError("%s must be [%d, %d, %d, %d]" % (name, rows, H, D, D))
     p.checkpoint_every_n_tokens = int(checkpoint_every_n_tokens)
+    state_tensor("state_checkpoints", state_checkpoints, written=True)
     if state_checkpoints is not None:
         if state_checkpoints.dtype not in _STATE_DTYPES or not state_checkpoints.is_contiguous():
             raise ValueError("state_checkpoints must be contiguous fp32/bf16/fp16")
@@ -180,6 +202,20 @@ def make_params(q, k, v, g=None, beta=None, scale=None, initial_state=None,
             raise ValueError("status must be an int32 tensor")
         p.status = _ptr(status)
     return p, output, output_state
+
+
+def workspace_tensor(workspace: Optional[torch.Tensor], device, need: int) -> torch.Tensor:
+    """The workspace a call uses: the caller's when it is a contiguous uint8
+    tensor on the call's device with at least ``need`` bytes, a fresh one when
+    the caller passed none or a smaller one.  Anything else raises: the
+    kernels take its address as device memory of the call's device."""
+    if workspace is not None:
+        if (workspace.device != torch.device(device) or workspace.dtype != torch.uint8
+                or not workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous uint8 tensor on %s" % device)
+        if workspace.numel() >= need:
+            return workspace
+    return torch.empty(need, dtype=torch.uint8, device=device)
 
 
 def workspace_size(p: nat.Params) -> int:
@@ -211,10 +247,9 @@ def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None,
     if need == 0:
         rc = lib.gdn_validate_host(ctypes.byref(p))
         _raise(rc if rc != 0 else nat.ERR_CODE["GDN_ERR_SHAPE"])
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = workspace_tensor(workspace, q.device, need)
     p.workspace = ctypes.c_void_p(workspace.data_ptr())
-    p.workspace_bytes = workspace.numel()
+    p.workspace_bytes = workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = lib.gdn_prefill(ctypes.byref(p), ctypes.c_void_p(stream))

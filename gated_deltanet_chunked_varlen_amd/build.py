@@ -1,5 +1,8 @@
 """Build libgdn_prefill.so in-tree with hipcc for gfx950.
 
+Each source compiles to its own object in parallel, then one link step makes
+the shared library.
+
 Usage: python -m gated_deltanet_chunked_varlen_amd.build
 """
 from __future__ import annotations
@@ -7,6 +10,8 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -22,21 +27,40 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def _clean(stderr: str) -> str:
+    return "\n".join(l for l in stderr.splitlines() if "packed-fp32-ops" not in l)
+
+
+def build(verbose: bool = False, extra_flags=None, out: str = LIB) -> str:
+    flags = FLAGS + list(extra_flags or [])
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-shared", "-o", tmp] + srcs
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in r.stderr.splitlines()
-                    if "packed-fp32-ops" not in l)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    with tempfile.TemporaryDirectory(prefix="gdn_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(s) + ".o") for s in srcs]
+
+        def compile_one(i):
+            cmd = [HIPCC] + flags + ["-c", srcs[i], "-o", objs[i]]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            return subprocess.run(cmd, capture_output=True, text=True)
+
+        jobs = max(1, min(len(srcs), os.cpu_count() or 1, 16))
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(compile_one, range(len(srcs))))
+        for s, r in zip(srcs, results):
+            err = _clean(r.stderr)
+            if r.returncode != 0:
+                raise RuntimeError("hipcc failed on %s:\n%s" % (os.path.basename(s), err))
+            if verbose and err.strip():
+                print(err, file=sys.stderr)
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [HIPCC] + flags + ["-shared", "-o", tmp] + objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + _clean(r.stderr))
+        os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

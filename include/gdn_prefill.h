@@ -158,16 +158,32 @@ const char *gdn_status_string(int code);
 int64_t gdn_max_chunks(int64_t total_tokens, int32_t num_seqs);
 
 /* Bytes of device workspace gdn_prefill() needs for these parameters (only
- * the shape fields are read).  Host only; 0 for an invalid shape. */
+ * the shape fields are read: token, sequence and head counts, head size,
+ * qkv dtype).  The pages' call allocates its scratch internally (gitcode,
+ * section "内部机制：plan 缓存、地址重绑定与 CUDA Graph": a cached plan
+ * holds the scratch of a shape); here the caller owns it, sized by this
+ * function, so a call never allocates.  Host only; 0 for an invalid shape. */
 size_t gdn_prefill_workspace_size(const gdn_prefill_params *p);
 
 /* Every host-side check of gdn_prefill() except the device check, without
- * touching the GPU.  Returns GDN_OK or a GDN_ERR_* code. */
+ * touching the GPU: the argument rules of gitcode, sections "API 全参数解析"
+ * (shapes, dtypes, head sharing, defaults), "状态池" (state_indices needs
+ * output_state and pool_size), "中间状态检查点" (n a multiple of 64, the two
+ * checkpoint buffers given together) and "约束与注意点" (max_seqlen within
+ * [ceil(T/N), T]), plus the workspace size and alignment.  Reads only the
+ * parameter block, never device memory.  Returns GDN_OK or the GDN_ERR_*
+ * code of the first failed check. */
 int gdn_validate_host(const gdn_prefill_params *p);
 
-/* The whole prefill: chunk-index build, intra-chunk pass, inter-chunk state
- * pass (with checkpoints and final/pool write-back), output pass.
- * Asynchronous on `stream`. */
+/* The whole prefill (gitcode, sections "GDN prefill" and "API 全参数解析";
+ * weigao.cc, "为什么要切成 64-token chunk"): the chunk-index build (large
+ * batches only), the intra-chunk pass (gate log-cumsum, A, T), and the fused
+ * pass that carries each state across chunks, writes checkpoints and the
+ * final state (pool row state_indices[i] when given), and forms the output.
+ * Runs gdn_validate_host() first and launches nothing when it fails.
+ * Asynchronous on `stream`; returns GDN_OK once everything is enqueued, or
+ * GDN_ERR_DEVICE (not a gfx950) / GDN_ERR_LAUNCH.  Data errors only the
+ * device can see set bits in *status. */
 int gdn_prefill(const gdn_prefill_params *p, void *stream);
 
 /* gdn_prefill() with phase markers: events[i] (a hipEvent_t, or NULL to

@@ -17,11 +17,12 @@ Three independent forms of the same definition live here:
 * ``exact_token`` -- the same recurrence in exact rational arithmetic
   (``fractions.Fraction``), for tiny sizes such as L = 8, D = 8, the first run
   0539edu "GDN与线性注意力GPU并行实现" section 3.1 recommends.
-* ``partial_transition`` -- the per-position partial transitions of 0539edu
-  section 3.2 (M_part, N_part accumulated inside each chunk, the chunk's last
-  pair carried to the next), with that section's transition read as
-  ``A_i = a_i (I - b_i k_i k_i^T)``, ``B_i = b_i k_i v_i^T`` and outputs
-  scaled by ``scale``.
+* ``partial_transition`` -- the pair-composition form of 0539edu sections
+  2.1-2.2: each position is an affine pair ``(A_i, B_i)`` with
+  ``A_i = a_i (I - b_i k_i k_i^T)``, ``B_i = b_i k_i v_i^T``; inside a chunk an
+  inclusive scan of the pairs gives every position's map from the chunk's
+  incoming state, and the chunk's composition carries the state on; outputs
+  are scaled by ``scale``.
 
 Parity is pinned for every function here by tests in ``tests/`` that check
 against the pages' printed examples, closed forms and exact arithmetic.  The
@@ -302,28 +303,36 @@ def exact_token(q, k, v, alpha, beta, scale, S0=None):
 # Page-3 partial transitions (tiny sizes only).
 # --------------------------------------------------------------------------
 
+def position_pair(k_i, v_i, alpha_i, beta_i):
+    """The affine map S -> A S + B of one position (0539edu section 2.1's
+    per-position transition pair, with the gate placement of reading R1):
+    A = alpha (I - beta k k^T), B = beta k v^T.  S is keys x values."""
+    k_i = np.asarray(k_i, np.float64)
+    D = k_i.shape[0]
+    A = alpha_i * (np.eye(D) - beta_i * np.outer(k_i, k_i))
+    return A, beta_i * np.outer(k_i, np.asarray(v_i, np.float64))
+
+
 def partial_transition(q, k, v, alpha, beta, scale, C, S0=None):
-    """One sequence, one head, fp64 numpy.  Inside each chunk the pairs
-    (M_part, N_part) start at (I, 0) and absorb each position's transition
-    (A_i, B_i); the position's output reads (M_part S + N_part); the chunk's
-    last pair moves the carried state to the next chunk (0539edu sections
-    2.1-2.2 and 3.2).  S is keys x values.  Returns (out [L,D], S_final)."""
+    """One sequence, one head, fp64 numpy, from pair composition (0539edu
+    sections 2.1-2.2 and 3.2): every position is an affine pair
+    (``position_pair``); inside a chunk the inclusive scan of the pairs under
+    ``combine_pairs`` gives, at each position, the map from the state that
+    entered the chunk to the state after that position, which the position's
+    output reads; the chunk's whole composition carries the state to the next
+    chunk.  Returns (out [L, D], S_final)."""
+    from itertools import accumulate
     q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
-    v = np.asarray(v, np.float64)
     L, D = q.shape
     S = np.zeros((D, D)) if S0 is None else np.array(S0, np.float64)
+    pairs = [position_pair(k[i], v[i], alpha[i], beta[i]) for i in range(L)]
     y = np.zeros((L, D))
     for start in range(0, L, C):
-        end = min(start + C, L)
-        Mp, Np = np.eye(D), np.zeros((D, D))
-        for i in range(start, end):
-            A = alpha[i] * (np.eye(D) - beta[i] * np.outer(k[i], k[i]))
-            B = beta[i] * np.outer(k[i], v[i])
-            Mp = A @ Mp
-            Np = A @ Np + B
-            y[i] = scale * (q[i] @ (Mp @ S + Np))
-        S = Mp @ S + Np
+        prefix = list(accumulate(pairs[start:start + C], combine_pairs))
+        for i, (M, N) in enumerate(prefix, start):
+            y[i] = scale * (q[i] @ (M @ S + N))
+        M, N = prefix[-1]
+        S = M @ S + N
     return y, S
 
 

@@ -218,3 +218,47 @@ def test_validate_decode_ok():
 ])
 def test_validate_decode_errors(kw, err):
     assert _validate_decode(_params(**kw)) == code(err)
+
+
+# ------------------------------------------------ binding argument checks
+
+def test_expanded_states_are_copied_or_rejected():
+    """An expanded state view (stride 0 on a dimension of extent > 1) aliases
+    its elements and would read as "contiguous" through the C ABI: a state the
+    library only reads is copied to contiguous memory first, one it writes is
+    refused before any launch."""
+    torch = pytest.importorskip("torch")
+    from gated_deltanet_chunked_varlen_amd import api
+    base = torch.zeros(())
+    view = base.expand(3, 2, 32, 32)
+    assert view.stride() == (0, 0, 0, 0)
+    got = api.state_tensor("initial_state", view, written=False)
+    assert got.is_contiguous() and got.stride() == (2048, 1024, 32, 1)
+    with pytest.raises(ValueError):
+        api.state_tensor("output_state", view, written=True)
+    # one broadcast dimension is enough
+    part = torch.zeros(1, 2, 32, 32).expand(4, 2, 32, 32)
+    with pytest.raises(ValueError):
+        api.state_tensor("state_checkpoints", part, written=True)
+    # ordinary, permuted and extent-1 zero-stride views pass through as they are
+    plain = torch.zeros(3, 2, 32, 32)
+    assert api.state_tensor("output_state", plain, written=True) is plain
+    perm = torch.zeros(2, 3, 32, 32).permute(1, 0, 2, 3)
+    assert api.state_tensor("output_state", perm, written=True) is perm
+    one = torch.zeros(1, 2, 32, 32).expand(1, 2, 32, 32)
+    assert api.state_tensor("output_state", one, written=True) is one
+
+
+def test_workspace_argument_checked():
+    torch = pytest.importorskip("torch")
+    from gated_deltanet_chunked_varlen_amd import api
+    ws = torch.zeros(100, dtype=torch.uint8)
+    assert api.workspace_tensor(ws, "cpu", 64) is ws
+    fresh = api.workspace_tensor(ws, "cpu", 256)        # too small: a new one
+    assert fresh is not ws and fresh.numel() == 256
+    with pytest.raises(ValueError):
+        api.workspace_tensor(torch.zeros(100, dtype=torch.float32), "cpu", 64)
+    with pytest.raises(ValueError):
+        api.workspace_tensor(torch.zeros(200, dtype=torch.uint8)[::2], "cpu", 64)
+    with pytest.raises(ValueError):
+        api.workspace_tensor(ws, "meta", 64)            # another device
