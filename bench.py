@@ -4,10 +4,19 @@
 A step is one full ``gdn_prefill`` call (chunk-index build where the batch
 needs it, intra-chunk pass, state pass with the output, all heads) over one
 batch of seeded synthetic input already resident in HBM; outputs and
-workspace are allocated once.  The
-default workload is 2 sequences x 2048 tokens, 16 heads, head size 128, bf16
-q/k/v with in-kernel q/k L2 normalisation (the shape of gitcode "FlashInfer
-GDN Prefill 完全指南", section "基础用法").
+workspace are allocated once.  The default workload is the GVA batch: 8
+sequences of seeded lengths in [1, 8192] (23,060 tokens), 16 q/k heads and 32
+v heads, head size 128, bf16 q/k/v with in-kernel q/k L2 normalisation,
+checkpoints every 1024 tokens and fp32 final states.  Beside it the same run
+times the 2 x 2048-token, 16-head batch (the shape of gitcode "FlashInfer GDN
+Prefill 完全指南", section "基础用法") and reports it under
+``"varlen_2x2048"``.
+
+The roofline fraction uses the method's own HBM bytes: q, k, v read and o
+written in the input dtype (shared q/k/v heads counted once per source head),
+g and beta in fp32, plus the initial, final and checkpoint states the call
+reads and writes.  The kernels' own bytes (intermediates included) are
+reported beside it as ``implementation_bytes_per_launch``.
 
 Prints one JSON line with the throughput (tokens/s over all heads, from K
 steps timed with nothing else in them), the roofline position of the
@@ -15,7 +24,7 @@ dominant kernel (timed live with HIP events recorded around it on the call's
 stream, in K further steps) and the CPU oracle's throughput on the same
 workload (a bounded number of repetitions on this host's cores).
 
-    python bench.py [--steps K] [--warmup W] [--workload varlen2x2048]
+    python bench.py [--steps K] [--warmup W] [--workload gva8]
     python bench.py --workload decode       # the decode step, its own line
     python bench.py --copy-calibration      # plain 1 GiB copies, for counters
     python bench.py --summarize <workload> <rocprofv3 output dirs...> <command>
@@ -40,6 +49,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak
 FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 matrix peak
 PHASES = ["chunk_index", "intra", "state", "output"]
+DEFAULT_WORKLOAD = "gva8"
+TRAFFIC_SOURCE = ("committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary (profiles/traffic.json), "
+                  "taken on the same kernel source (hash-matched); not measured in this run")
 KERNEL_SOURCES = {
     "chunk_index": "k0_chunk_index.hip", "intra": "k1_intra.hip",
     "state": "k2_state.hip", "output": "k3_output.hip", "decode": "k4_decode.hip",
@@ -82,6 +94,43 @@ def per_token_head_bytes(wl, phase):
     if phase == "output":
         return (qf + kf) * D * e + st + D * e + 4 + D * e
     return 0.0
+
+
+STATE_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "e4m3": 1, "e5m2": 1}
+
+
+def method_bytes(wl):
+    """The method's HBM bytes for one call, independent of how the kernels
+    split the work: per (token, sab head) q, k and v read and o written in
+    the input dtype (shared heads counted once per source head) and g, beta
+    in fp32 -- 1,032 B with equal heads at D = 128 in bf16, 776 B with 16
+    q/k heads and 32 v heads -- plus, per (sequence, head), the initial state
+    read, the final state written and every checkpoint row written."""
+    D, H, T, N = wl.D, wl.H, wl.T, wl.N
+    e = 4 if wl.dtype == "f32" else 2
+    hq, hk, hv = wl.q.shape[1], wl.k.shape[1], wl.v.shape[1]
+    per_th = (hq + hk + hv) / H * D * e + D * e + (8 if wl.g is not None else 0)
+    total = per_th * T * H
+    st = D * D * H
+    if wl.initial_state is not None:
+        total += N * st * STATE_BYTES[wl.initial_state_dtype]
+    if wl.output_final_state:
+        total += N * st * STATE_BYTES[wl.final_state_dtype]
+    if wl.checkpoint_every > 0 and wl.checkpoint_cu_starts is not None:
+        total += int(wl.checkpoint_cu_starts[-1]) * st * STATE_BYTES[wl.checkpoint_dtype]
+    return float(total)
+
+
+def cpu_model():
+    """The host CPU's model name (lscpu's "Model name", from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 FLOPS_PER_TOKEN_HEAD = lambda D: 2 * (5 * 64 * D + 3 * D * D)   # eight chunk GEMMs
@@ -181,7 +230,7 @@ def cpu_baseline(wl, seconds):
             break
     items = wl.N * wl.H
     return {"value": wl.T * reps / dt, "unit": "tokens/s",
-            "cores": min(oracle.num_threads(), items), "kind": "oracle",
+            "cores": min(oracle.num_threads(), items), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "whole workload (%d tokens x %d heads), fp64 token "
                       "recurrence, %d repetition(s) in %.1f s" % (
                           wl.T, wl.H, reps, dt)}
@@ -430,54 +479,16 @@ def bench_decode(args):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
-        summarize(sys.argv[2:])
-        return
-    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-mfma":
-        summarize_mfma(sys.argv[2:])
-        return
-    ap = argparse.ArgumentParser(description=__doc__,
-                                 formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--workload", default="varlen2x2048",
-                    help="varlen2x2048 (default, the headline); single128, "
-                         "ragged6, gva8, long262144 for analysis; decode for "
-                         "the decode step (its own JSON line)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--cold-calls", type=int, default=20,
-                    help="calls timed after flushing the last-level cache (0: none)")
-    args = ap.parse_args()
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        if int(os.environ.get("RANK", "0")) == 0:
-            print("bench.py: the library runs on one GPU only (more GPUs would "
-                  "take whole sequences or heads each, with no communication); "
-                  "--gpus %d is not supported" % args.gpus,
-                  file=sys.stderr)
-        sys.exit(2)
-
+def measure_prefill(wl, steps, warmup, cold_calls):
+    """Time one prefill workload: throughput over exactly ``steps`` calls after
+    ``warmup`` untimed ones, per-phase times, the dominant kernel timed with
+    HIP events on the call's stream, optionally cold-cache calls.  Returns a
+    dict of the raw figures."""
     import torch
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.workload == "decode":
-        bench_decode(args)
-        return
-
     from gated_deltanet_chunked_varlen_amd import workloads as W
     from gated_deltanet_chunked_varlen_amd import api
     from gated_deltanet_chunked_varlen_amd import _native as nat
 
-    wl = W.WORKLOADS[args.workload]()
     d = W.to_device(wl)
     H, D, N, T = wl.H, wl.D, wl.N, wl.T
     kw = dict(g=d["g"], beta=d["beta"], scale=wl.scale, cu_seqlens=d["cu_seqlens"],
@@ -511,7 +522,7 @@ def main():
     # dominant kernel afterwards).  The timed region follows at once: after a
     # few ms of idleness the GPU clock drops and needs ~10 ms of work to come
     # back, so nothing (no event reads) may sit between the two.
-    W_ = max(args.warmup, 1)
+    W_ = max(warmup, 1)
     n_ev = min(W_, 50)
     ev = [[new_event(L) for _ in range(5)] for _ in range(n_ev)]
     for i in range(W_):
@@ -519,7 +530,7 @@ def main():
         call((ctypes.c_void_p * 5)(*ev[j]) if j >= 0 else none5)
 
     # timed region: exactly K steps, each the call as a user makes it
-    K = args.steps
+    K = steps
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -569,11 +580,11 @@ def main():
     # call, as a write would), and the call alone is timed between the first
     # and last of its phase events
     cold = None
-    if args.cold_calls > 0:
+    if cold_calls > 0:
         flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
-        ce = [(new_event(L), new_event(L)) for _ in range(args.cold_calls)]
-        for i in range(args.cold_calls):
+        ce = [(new_event(L), new_event(L)) for _ in range(cold_calls)]
+        for i in range(cold_calls):
             flush.sum()
             e5 = (ctypes.c_void_p * 5)()
             e5[0], e5[4] = ce[i][0], ce[i][1]
@@ -585,8 +596,17 @@ def main():
             L.hipEventDestroy(b)
         del flush
         cold = {"ms_per_call_median": cms, "tokens_per_s": T / (cms / 1e3),
-                "flush_read_bytes": 512 << 20, "calls": args.cold_calls}
+                "flush_read_bytes": 512 << 20, "calls": cold_calls}
 
+    return dict(wl=wl, ms_total=ms_total, K=K, wall=wall, phase_ms=phase_ms, dom=dom,
+                dom_ms=dom_ms, cold=cold)
+
+
+def prefill_record(m):
+    """The figures of one measured prefill workload (measure_prefill)."""
+    wl = m["wl"]
+    H, D, N, T = wl.H, wl.D, wl.N, wl.T
+    K, ms_total, phase_ms, dom, dom_ms = m["K"], m["ms_total"], m["phase_ms"], m["dom"], m["dom_ms"]
     ms_step = ms_total / K
     tokens_per_s = T * K / (ms_total / 1e3)
     # the whole call: counter-measured HBM bytes of every kernel it launches
@@ -599,22 +619,100 @@ def main():
         tb = sum(known.values())
         gbs = tb / (ms_step / 1e3) / 1e9
         call_traffic = {"bytes": tb, "phases": sorted(known), "achieved": gbs,
-                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                        "source": TRAFFIC_SOURCE}
     flops = T * H * FLOPS_PER_TOKEN_HEAD(D)
     tflops = flops / (ms_step / 1e3) / 1e12
     peak_mm = FP32_PEAK_TFLOPS if wl.dtype == "f32" else BF16_PEAK_TFLOPS   # fp16 peak = bf16 peak
-    bytes_launch = per_token_head_bytes(wl, dom) * T * H
-    achieved = bytes_launch / (dom_ms / 1e3) / 1e9
+    mbytes = method_bytes(wl)
+    achieved = mbytes / (dom_ms / 1e3) / 1e9
+    impl_bytes = per_token_head_bytes(wl, dom) * T * H
     traffic = load_traffic(dom, wl.name)
+    return {
+        "ms_per_step": ms_step,
+        "tokens_per_s": tokens_per_s,
+        "tflops_canonical": tflops,
+        "tflops_triangle": T * H * FLOPS_TRI_PER_TOKEN_HEAD(D) / (ms_step / 1e3) / 1e12,
+        "mfma_peak_frac": tflops / peak_mm,
+        "phase_ms_warmup": phase_ms,
+        "mfma_counters": load_mfma(wl.name) or None,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "traffic_source": TRAFFIC_SOURCE if traffic else None,
+                     "avg_launch_ms": dom_ms,
+                     "timing": "HIP events around the kernel in each of K further steps",
+                     "algorithmic_bytes_per_launch": mbytes,
+                     "algorithmic_bytes_model": "method bytes of the whole call (q, k, v, o, "
+                                                "g, beta, states, checkpoints) over the "
+                                                "dominant kernel's time",
+                     "implementation_bytes_per_launch": impl_bytes,
+                     "implementation_frac": impl_bytes / (dom_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "call_hbm_frac_method_bytes": mbytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "cold_cache": m["cold"],
+        "call_traffic": call_traffic,
+        "wall_s_timed": m["wall"],
+    }
 
+
+def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
+        summarize(sys.argv[2:])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-mfma":
+        summarize_mfma(sys.argv[2:])
+        return
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="gva8 (default, the headline; also times varlen2x2048 "
+                         "under \"varlen_2x2048\"); varlen2x2048, single128, "
+                         "ragged6, long262144 alone; decode for the decode step "
+                         "(its own JSON line)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="with the default workload, skip the 2 x 2048 figures")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="calls timed after flushing the last-level cache (0: none)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py: the library runs on one GPU only (more GPUs would "
+                  "take whole sequences or heads each, with no communication); "
+                  "--gpus %d is not supported" % args.gpus,
+                  file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.workload == "decode":
+        bench_decode(args)
+        return
+
+    from gated_deltanet_chunked_varlen_amd import workloads as W
+    wl = W.WORKLOADS[args.workload]()
+    m = measure_prefill(wl, args.steps, args.warmup, args.cold_calls)
+    r = prefill_record(m)
+    H, D, N, T = wl.H, wl.D, wl.N, wl.T
     res = {
         "metric": "GDN prefill tokens/s (all heads) + % of MI355X bf16 MFMA peak, H=16 D=128",
-        "value": tokens_per_s,
+        "value": r["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -624,21 +722,20 @@ def main():
                    "total_tokens": T, "num_q_heads": int(wl.q.shape[1]),
                    "num_k_heads": int(wl.k.shape[1]), "num_v_heads": int(wl.v.shape[1]),
                    "head_size": D, "qk_l2norm_in_kernel": wl.l2norm_in_kernel,
+                   "checkpoint_every_n_tokens": wl.checkpoint_every,
                    "parallelism": "single GPU"},
-        "tflops_canonical": tflops,
-        "tflops_triangle": T * H * FLOPS_TRI_PER_TOKEN_HEAD(D) / (ms_step / 1e3) / 1e12,
-        "mfma_peak_frac": tflops / peak_mm,
-        "phase_ms_warmup": phase_ms,
-        "mfma_counters": load_mfma(wl.name) or None,
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "avg_launch_ms": dom_ms,
-                     "timing": "HIP events around the kernel in each of K further steps",
-                     "algorithmic_bytes_per_launch": bytes_launch},
-        "wall_s_timed": wall,
-        "cold_cache": cold,
-        "call_traffic": call_traffic,
     }
+    res.update({k: v for k, v in r.items() if k not in ("ms_per_step", "tokens_per_s")})
+    if args.workload == DEFAULT_WORKLOAD and not args.no_extra:
+        # the 2 x 2048-token, 16-head batch, timed the same way in this run
+        w2 = W.WORKLOADS["varlen2x2048"]()
+        r2 = prefill_record(measure_prefill(w2, args.steps, min(args.warmup, 500), 0))
+        res["varlen_2x2048"] = {
+            "workload": w2.name, "ms_per_step": r2["ms_per_step"],
+            "tokens_per_s": r2["tokens_per_s"], "tflops_canonical": r2["tflops_canonical"],
+            "mfma_peak_frac": r2["mfma_peak_frac"], "phase_ms_warmup": r2["phase_ms_warmup"],
+            "roofline": r2["roofline"],
+            "call_hbm_frac_method_bytes": r2["call_hbm_frac_method_bytes"]}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)

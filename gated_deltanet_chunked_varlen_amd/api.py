@@ -16,6 +16,7 @@ library or a gfx950 device the call raises.
 from __future__ import annotations
 
 import ctypes
+from collections import OrderedDict
 from typing import Optional
 
 import torch
@@ -218,6 +219,40 @@ def workspace_tensor(workspace: Optional[torch.Tensor], device, need: int) -> to
     return torch.empty(need, dtype=torch.uint8, device=device)
 
 
+# ---------------------------------------------------------------------------
+# Plan / workspace cache (gitcode "FlashInfer GDN Prefill 完全指南", section
+# "内部机制：plan 缓存、地址重绑定与 CUDA Graph": the dispatcher keeps the
+# shape-dependent plan and workspace and launches directly, so outputs the API
+# allocates and rotating input buffers may change address without a new plan).
+# Here the plan is the workspace layout the library derives from the shape on
+# every call (host arithmetic only); what is worth keeping is the workspace.
+# One workspace per (device, stream): calls on one stream run in order and can
+# share it; calls on different streams get their own.  It grows to the largest
+# call seen and is released with clear_workspace_cache().
+# ---------------------------------------------------------------------------
+_WS_CACHE_MAX = 64
+_ws_cache: "OrderedDict[tuple, torch.Tensor]" = OrderedDict()
+
+
+def cached_workspace(device, stream: int, need: int) -> torch.Tensor:
+    """The cached workspace of (device, stream), grown to at least ``need``
+    bytes (least recently used entries beyond 64 are dropped)."""
+    dev = torch.device(device)
+    key = (dev.type, dev.index, int(stream))
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = ws
+    _ws_cache.move_to_end(key)
+    while len(_ws_cache) > _WS_CACHE_MAX:
+        _ws_cache.popitem(last=False)
+    return ws
+
+
+def clear_workspace_cache() -> None:
+    _ws_cache.clear()
+
+
 def workspace_size(p: nat.Params) -> int:
     return int(nat.lib().gdn_prefill_workspace_size(ctypes.byref(p)))
 
@@ -235,7 +270,8 @@ def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None,
     g, beta [T, H] float32 (H = max(hq, hv)); cu_seqlens [N+1] int32/int64;
     states [N or pool, H, D(v), D(k)].  ``status`` (optional int32 device
     tensor) receives the device-side check bits.  ``workspace`` (optional
-    uint8 device tensor) is used instead of a fresh allocation.
+    uint8 device tensor) is used instead of the workspace cached for the
+    current (device, stream).
     """
     lib = nat.lib()
     p, output, output_state = make_params(
@@ -247,11 +283,18 @@ def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None,
     if need == 0:
         rc = lib.gdn_validate_host(ctypes.byref(p))
         _raise(rc if rc != 0 else nat.ERR_CODE["GDN_ERR_SHAPE"])
-    workspace = workspace_tensor(workspace, q.device, need)
-    p.workspace = ctypes.c_void_p(workspace.data_ptr())
-    p.workspace_bytes = workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
+        if workspace is None and torch.cuda.is_current_stream_capturing():
+            # a graph keeps the address it was captured with: give it memory of
+            # its own capture pool rather than the shared cached workspace
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        elif workspace is None:
+            workspace = cached_workspace(q.device, stream, need)
+        else:
+            workspace = workspace_tensor(workspace, q.device, need)
+        p.workspace = ctypes.c_void_p(workspace.data_ptr())
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
         rc = lib.gdn_prefill(ctypes.byref(p), ctypes.c_void_p(stream))
     if rc != 0:
         _raise(rc)
@@ -312,3 +355,76 @@ def build_chunk_indices(cu_seqlens: Optional[torch.Tensor], total_tokens: int,
     if rc != 0:
         _raise(rc)
     return table[:cap], cu_chunks, starts, n, st
+
+
+# ---------------------------------------------------------------------------
+# Graph replay with rotating buffers (gitcode, section "内部机制：plan 缓存、
+# 地址重绑定与 CUDA Graph": fixed-address prepared calls replay from a CUDA
+# graph, captured on the first call only).  A captured graph holds the
+# addresses it was captured with, so this cache keeps one executable graph per
+# address set: a caller that rotates among a few sets of q/k/v/output buffers
+# (double or triple buffering) captures each set once and replays it after.
+# Metadata needs no host-side resolution before capture: the chunk table is
+# built on the device inside the call.
+# ---------------------------------------------------------------------------
+class PrefillGraphs:
+    """``chunk_gated_delta_rule`` through HIP graphs, one per distinct set of
+    tensor addresses and sizes (at most ``max_graphs``, least recently used
+    dropped).  Call it with the arguments of ``chunk_gated_delta_rule``;
+    ``output`` (and ``output_state`` with ``output_final_state``) must be
+    given, since a replay writes into the buffers it was captured with.  The
+    first call with a new address set runs the call once eagerly (on a side
+    stream, to load the library and build its workspace) and captures it;
+    every call replays the graph of its address set on the current stream.
+    ``graphs_captured`` counts captures."""
+
+    def __init__(self, max_graphs: int = 16):
+        self.max_graphs = max_graphs
+        self._graphs: "OrderedDict[tuple, tuple]" = OrderedDict()
+        self.graphs_captured = 0
+
+    @staticmethod
+    def _key(args, kwargs):
+        parts = []
+        for x in list(args) + [kwargs[k] for k in sorted(kwargs)]:
+            if isinstance(x, torch.Tensor):
+                parts.append(("t", x.data_ptr(), tuple(x.shape), tuple(x.stride()), str(x.dtype),
+                              str(x.device)))
+            else:
+                parts.append(("v", repr(x)))
+        return tuple(sorted(kwargs)), tuple(parts)
+
+    def __call__(self, *args, **kwargs):
+        if kwargs.get("output") is None:
+            raise ValueError("PrefillGraphs needs an explicit output buffer")
+        if kwargs.get("output_final_state") and kwargs.get("output_state") is None:
+            raise ValueError("PrefillGraphs needs an explicit output_state buffer")
+        if len(args) > 18:
+            raise ValueError("pass workspace by keyword")
+        kwargs = {k: v for k, v in kwargs.items() if k != "workspace"}
+        key = self._key(args, kwargs)
+        hit = self._graphs.get(key)
+        if hit is None:
+            # each graph owns its workspace, so graphs of different address
+            # sets and eager calls never share one
+            p, _, _ = make_params(*args, **kwargs)
+            ws = torch.empty(max(workspace_size(p), 1), dtype=torch.uint8,
+                             device=args[0].device)
+            kwargs_ws = dict(kwargs, workspace=ws)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                chunk_gated_delta_rule(*args, **kwargs_ws)
+            torch.cuda.current_stream().wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                res = chunk_gated_delta_rule(*args, **kwargs_ws)
+            hit = (graph, res, ws)
+            self._graphs[key] = hit
+            self.graphs_captured += 1
+            while len(self._graphs) > self.max_graphs:
+                self._graphs.popitem(last=False)
+        self._graphs.move_to_end(key)
+        graph, res, _ = hit
+        graph.replay()
+        return res

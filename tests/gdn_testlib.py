@@ -162,26 +162,89 @@ def run_gpu_decode(wl, device="cuda", status=False, **over):
     return r
 
 
+def block_max_rel_l2(x, ref, blocks):
+    """Largest relative L2 error over the given blocks: ``blocks`` is a list
+    of index expressions into the leading axes of x / ref.  A block's error
+    is ||x_b - ref_b|| over the larger of ||ref_b|| and the norm the block
+    would have at the whole tensor's root-mean-square value.  The floor is
+    what the rounding of the inputs allows: a dot product of rounded operands
+    errs in proportion to the sum of the magnitudes of its terms, not to its
+    value, so a block whose true values nearly cancel (a one-token output
+    whose q and k are nearly orthogonal) is held to the tensor's scale.  A
+    block that is wrong at the tensor's scale (zeroed, swapped, misplaced)
+    still reads close to 1.  Returns (error, the block where it occurs)."""
+    ref = np.asarray(ref, np.float64)
+    x = np.asarray(x, np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    worst, where = 0.0, None
+    for b in blocks:
+        rb, xb = ref[b], x[b]
+        den = max(float(np.linalg.norm(rb)), rms * np.sqrt(rb.size))
+        e = float(np.linalg.norm(xb - rb)) / den if den > 0 else float(np.linalg.norm(xb))
+        if e > worst:
+            worst, where = e, b
+    return worst, where
+
+
+def chunk_blocks(cu, H, C=64):
+    """(token slice, head) of every C-token chunk of every sequence (chunks
+    start at each sequence's first token) and every head."""
+    cu = np.asarray(cu, np.int64)
+    out = []
+    for i in range(len(cu) - 1):
+        for t0 in range(int(cu[i]), int(cu[i + 1]), C):
+            t1 = min(t0 + C, int(cu[i + 1]))
+            out.extend((slice(t0, t1), h) for h in range(H))
+    return out
+
+
+def sequence_blocks(cu):
+    cu = np.asarray(cu, np.int64)
+    return [slice(int(cu[i]), int(cu[i + 1])) for i in range(len(cu) - 1)
+            if cu[i + 1] > cu[i]]
+
+
 def compare(wl, gpu, orc, heads=None):
-    """Relative L2 errors of outputs / final states / checkpoints."""
+    """Relative L2 errors of outputs / final states / checkpoints, each over
+    the whole tensor and, as "<name>_block", the largest over every
+    (64-token chunk, head) block and every sequence of the output, every
+    (sequence, head) of the final state and every (row, head) of the
+    checkpoints: a wrong chunk, head or row cannot hide in a large tensor."""
     tol = TOL[wl.dtype]
     sel = (lambda x: x) if heads is None else (lambda x: x[:, heads])
-    errs = {"out": rel_l2(sel(gpu["out"]), orc["out"])}
+    go = sel(gpu["out"])
+    ro = orc["out"]
+    nh = ro.shape[1]
+    errs = {"out": rel_l2(go, ro)}
+    e1, _ = block_max_rel_l2(go, ro, chunk_blocks(wl.cu_seqlens, nh))
+    e2, _ = block_max_rel_l2(go, ro, sequence_blocks(wl.cu_seqlens))
+    errs["out_block"] = max(e1, e2)
     if wl.output_final_state:
         if wl.state_indices is not None:
             idx = [int(r) for r in wl.state_indices]
-            errs["final"] = rel_l2(sel(gpu["final"][idx]), orc["final"])
+            gf = sel(gpu["final"][idx])
         else:
-            errs["final"] = rel_l2(sel(gpu["final"]), orc["final"])
+            gf = sel(gpu["final"])
+        rf = orc["final"]
+        errs["final"] = rel_l2(gf, rf)
+        nz = [(i, h) for i in range(rf.shape[0]) for h in range(nh)
+              if np.any(rf[i, h] != 0)]
+        errs["final_block"] = block_max_rel_l2(gf, rf, nz)[0] if nz else 0.0
     if wl.checkpoint_every > 0 and orc["ckpt"] is not None and orc["ckpt"].size:
-        errs["ckpt"] = rel_l2(sel(gpu["ckpt"]), orc["ckpt"])
+        gc, rc = sel(gpu["ckpt"]), orc["ckpt"]
+        errs["ckpt"] = rel_l2(gc, rc)
+        errs["ckpt_block"] = block_max_rel_l2(
+            gc, rc, [(r, h) for r in range(rc.shape[0]) for h in range(nh)])[0]
     return errs, tol
 
 
 def bars(wl):
     """The relative-L2 bar of each compared tensor: the compute bar, plus the
-    store rounding for states kept in a type narrower than fp32."""
+    store rounding for states kept in a type narrower than fp32.  The block
+    maxima (``*_block``) take the same bars."""
     tol = TOL[wl.dtype]
-    return {"out": tol,
-            "final": tol + STORE_TOL.get(wl.final_state_dtype, 0.0),
-            "ckpt": tol + STORE_TOL.get(wl.checkpoint_dtype, 0.0)}
+    b = {"out": tol,
+         "final": tol + STORE_TOL.get(wl.final_state_dtype, 0.0),
+         "ckpt": tol + STORE_TOL.get(wl.checkpoint_dtype, 0.0)}
+    b.update({k + "_block": v for k, v in list(b.items())})
+    return b

@@ -113,3 +113,92 @@ def test_decode_graph_loop_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(got, out)
         assert torch.equal(pool_g, pool_e)
+
+
+def _buffer_set(seed, lengths, H, D, mk):
+    d = tl.to_device(mk(seed))
+    N, T = len(lengths), sum(lengths)
+    d["out"] = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    d["fin"] = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
+    d["st"] = torch.empty(1, dtype=torch.int32, device="cuda")
+    return d
+
+
+def _args(d):
+    return dict(initial_state=d["initial_state"], output_final_state=True,
+                cu_seqlens=d["cu_seqlens"], use_qk_l2norm_in_kernel=True,
+                output=d["out"], output_state=d["fin"], status=d["st"])
+
+
+def test_rotating_buffer_sets_replay_bit_equal_to_eager():
+    # gitcode "FlashInfer GDN Prefill 完全指南", section "内部机制：plan 缓存、
+    # 地址重绑定与 CUDA Graph": three sets of q/k/v/output buffers used in
+    # turn (triple buffering); each set is captured once and replayed after,
+    # with new contents, eager work and synchronisation between replays
+    lengths, H, D = [130, 20, 300, 1, 64], 4, 128
+    mk = lambda seed: W.make(seed, lengths, H, H, H, D, "bf16", l2norm_in_kernel=True,
+                             init="seq", init_std=0.3)
+    sets = [_buffer_set(70 + i, lengths, H, D, mk) for i in range(3)]
+    assert len({s["q"].data_ptr() for s in sets}) == 3
+    assert len({s["out"].data_ptr() for s in sets}) == 3
+    graphs = api.PrefillGraphs()
+    seed = 80
+    for rnd in range(3):
+        for s in sets:
+            _refill(s, mk(seed))
+            seed += 1
+            got_out, got_fin = graphs(s["q"], s["k"], s["v"], s["g"], s["beta"], **_args(s))
+            assert got_out.data_ptr() == s["out"].data_ptr()
+            torch.cuda.synchronize()
+            got_out, got_fin, got_st = got_out.clone(), got_fin.clone(), int(s["st"].item())
+            # eager work between replays: an unrelated product and a call
+            # into fresh output buffers through the cached workspace
+            junk = torch.randn(256, 256, device="cuda") @ torch.randn(256, 256, device="cuda")
+            e_out, e_fin = chunk_gated_delta_rule(
+                s["q"], s["k"], s["v"], s["g"], s["beta"],
+                initial_state=s["initial_state"], output_final_state=True,
+                cu_seqlens=s["cu_seqlens"], use_qk_l2norm_in_kernel=True)
+            torch.cuda.synchronize()
+            del junk
+            assert got_st == 0
+            assert torch.equal(got_out, e_out), (rnd, seed)
+            assert torch.equal(got_fin, e_fin), (rnd, seed)
+    assert graphs.graphs_captured == 3
+
+
+def test_workspace_cache_reused_across_rotating_buffers():
+    # the plan's workspace is kept per (device, stream): calls whose tensors
+    # change address reuse it, a larger call grows it, another stream gets its
+    # own, and results match calls given a fresh workspace of their own
+    api.clear_workspace_cache()
+    lengths, H, D = [300, 64, 17], 4, 128
+    mk = lambda seed: W.make(seed, lengths, H, H, H, D, "bf16", l2norm_in_kernel=True,
+                             init="seq", init_std=0.3)
+    ptrs = set()
+    for i in range(3):
+        s = tl.to_device(mk(90 + i))
+        got = chunk_gated_delta_rule(s["q"], s["k"], s["v"], s["g"], s["beta"],
+                                     initial_state=s["initial_state"],
+                                     cu_seqlens=s["cu_seqlens"], use_qk_l2norm_in_kernel=True)
+        ptrs.add(tuple(w.data_ptr() for w in api._ws_cache.values()))
+        p, _, _ = api.make_params(s["q"], s["k"], s["v"], s["g"], s["beta"],
+                                  initial_state=s["initial_state"],
+                                  cu_seqlens=s["cu_seqlens"], use_qk_l2norm_in_kernel=True)
+        ws = torch.zeros(api.workspace_size(p), dtype=torch.uint8, device="cuda")
+        ref = chunk_gated_delta_rule(s["q"], s["k"], s["v"], s["g"], s["beta"],
+                                     initial_state=s["initial_state"],
+                                     cu_seqlens=s["cu_seqlens"], use_qk_l2norm_in_kernel=True,
+                                     workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref)
+    assert len(ptrs) == 1 and len(api._ws_cache) == 1
+    big = tl.to_device(W.make(95, [4096], H, H, H, D, "bf16", l2norm_in_kernel=True))
+    chunk_gated_delta_rule(big["q"], big["k"], big["v"], big["g"], big["beta"],
+                           cu_seqlens=big["cu_seqlens"], use_qk_l2norm_in_kernel=True)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        chunk_gated_delta_rule(big["q"], big["k"], big["v"], big["g"], big["beta"],
+                               cu_seqlens=big["cu_seqlens"], use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    assert len(api._ws_cache) == 2
+    api.clear_workspace_cache()
