@@ -19,7 +19,9 @@ ERRORS = {
     -4: "GDN_ERR_DTYPE", -5: "GDN_ERR_CHECKPOINT", -6: "GDN_ERR_STATE",
     -7: "GDN_ERR_MAX_SEQLEN", -8: "GDN_ERR_WORKSPACE", -9: "GDN_ERR_STRIDES",
     -10: "GDN_ERR_DEVICE", -11: "GDN_ERR_LAUNCH", -12: "GDN_ERR_ALIGN",
+    -13: "GDN_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 128 << 20
 ERR_CODE = {v: k for k, v in ERRORS.items()}
 STATUS_CU_SEQLENS = 1
 STATUS_CHECKPOINT_STARTS = 2
@@ -31,7 +33,7 @@ EXPORTS = [
     "gdn_abi_version", "gdn_status_string", "gdn_max_chunks",
     "gdn_prefill_workspace_size", "gdn_validate_host", "gdn_prefill",
     "gdn_prefill_timed", "gdn_build_chunk_indices", "gdn_decode",
-    "gdn_validate_decode_host",
+    "gdn_validate_decode_host", "gdn_prefill_noalloc",
 ]
 
 _i64x4 = ctypes.c_int64 * 4
@@ -107,6 +109,8 @@ def lib():
         L.gdn_prefill_timed.restype = ctypes.c_int
         L.gdn_prefill_timed.argtypes = [ctypes.POINTER(Params), ctypes.c_void_p,
                                         ctypes.c_void_p * 5]
+        L.gdn_prefill_noalloc.restype = ctypes.c_int
+        L.gdn_prefill_noalloc.argtypes = [ctypes.POINTER(Params), ctypes.c_void_p]
         L.gdn_decode.restype = ctypes.c_int
         L.gdn_decode.argtypes = [ctypes.POINTER(Params), ctypes.c_void_p]
         L.gdn_validate_decode_host.restype = ctypes.c_int

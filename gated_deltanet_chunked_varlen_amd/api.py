@@ -303,6 +303,41 @@ def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None,
     return output
 
 
+def chunk_gated_delta_rule_noalloc(q, k, v, g=None, beta=None, scale=None,
+                                   initial_state=None, output_final_state=False,
+                                   cu_seqlens=None, use_qk_l2norm_in_kernel=False,
+                                   output=None, output_state=None,
+                                   state_checkpoints=None, checkpoint_cu_starts=None,
+                                   checkpoint_every_n_tokens=0, state_indices=None,
+                                   max_seqlen=None, status=None):
+    """``chunk_gated_delta_rule`` through gdn_prefill_noalloc: the library's
+    static device scratch (128 MiB per GPU) serves as the workspace and
+    nothing is allocated, here or in the library.  ``output`` (and
+    ``output_state`` with ``output_final_state``) must be given, and an
+    expanded ``initial_state`` is refused rather than copied.  Calls that
+    overlap in time on one GPU race on the shared scratch."""
+    if output is None:
+        raise ValueError("the no-allocation call needs an output buffer")
+    if output_final_state and output_state is None:
+        raise ValueError("the no-allocation call needs an output_state buffer")
+    if initial_state is not None and _broadcast(initial_state):
+        raise ValueError("initial_state must not be an expanded view here")
+    lib = nat.lib()
+    p, output, output_state = make_params(
+        q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
+        use_qk_l2norm_in_kernel, output, output_state, state_checkpoints,
+        checkpoint_cu_starts, checkpoint_every_n_tokens, state_indices,
+        max_seqlen, status)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.gdn_prefill_noalloc(ctypes.byref(p), ctypes.c_void_p(stream))
+    if rc != 0:
+        _raise(rc)
+    if output_final_state:
+        return output, output_state
+    return output
+
+
 def gated_delta_rule_decode(q, k, v, g=None, beta=None, scale=None,
                             initial_state=None, output_final_state=True,
                             use_qk_l2norm_in_kernel=False, output=None,

@@ -152,6 +152,7 @@ const char *gdn_status_string(int code) {
     case GDN_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
     case GDN_ERR_LAUNCH: return "kernel launch failed";
     case GDN_ERR_ALIGN: return "q, k, v and output must be 16-byte aligned and the workspace 256-byte aligned";
+    case GDN_ERR_SCRATCH: return "gdn_prefill_noalloc: the call needs more workspace than the static scratch (GDN_NOALLOC_SCRATCH_BYTES) or its address is unavailable";
     case (int)GDN_STATUS_CU_SEQLENS: return "status: cu_seqlens not non-decreasing within [0, total_tokens]";
     case (int)GDN_STATUS_CHECKPOINT_STARTS: return "status: checkpoint_cu_starts differs from the prefix sum of floor(len / n)";
     case (int)GDN_STATUS_STATE_INDEX: return "status: a state index is outside [0, pool_size)";
@@ -372,6 +373,47 @@ static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *
 
 int gdn_prefill(const gdn_prefill_params *p, void *stream) {
   return prefill_impl(p, stream, nullptr);
+}
+
+// The no-allocation variant's workspace: one copy per GPU, created when the
+// code object is loaded on that GPU.  In host code `scratch` is only a
+// stand-in for the symbol; its device address comes from hipGetSymbolAddress,
+// looked up once per device and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+static int scratch_address(void **out) {
+  static std::mutex mu;
+  static void *scratch_ptr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GDN_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return GDN_ERR_SCRATCH;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return GDN_OK;
+}
+
+int gdn_prefill_noalloc(const gdn_prefill_params *p, void *stream) {
+  if (!p) return GDN_ERR_NULL;
+  gdn_prefill_params q = *p;
+  q.workspace = nullptr;
+  q.workspace_bytes = 0;
+  const size_t need = gdn_prefill_workspace_size(&q);
+  if (need == 0) {
+    const int rc = gdn_validate_host(&q);
+    return rc != GDN_OK ? rc : GDN_ERR_SHAPE;
+  }
+  if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_SCRATCH;
+  int rc = check_device();
+  if (rc != GDN_OK) return rc;
+  rc = scratch_address(&q.workspace);
+  if (rc != GDN_OK) return rc;
+  q.workspace_bytes = GDN_NOALLOC_SCRATCH_BYTES;
+  return prefill_impl(&q, stream, nullptr);
 }
 
 int gdn_validate_decode_host(const gdn_prefill_params *p) {

@@ -69,6 +69,13 @@ typedef enum { GDN_I32 = 0, GDN_I64 = 1 } gdn_itype;
 #define GDN_ERR_ALIGN -12        /* q, k, v or output not 16-byte aligned, or the
                                     workspace not 256-byte aligned (the kernels
                                     move them in 16-byte vector accesses) */
+#define GDN_ERR_SCRATCH -13      /* gdn_prefill_noalloc(): the call needs more
+                                    workspace than GDN_NOALLOC_SCRATCH_BYTES, or
+                                    the static scratch's address is unavailable */
+
+/* Size of the static device scratch that gdn_prefill_noalloc() uses in place
+ * of a workspace (one copy per GPU, held until the process ends). */
+#define GDN_NOALLOC_SCRATCH_BYTES (128u << 20)
 
 /* Device status bits (written to *status by every call). */
 #define GDN_STATUS_CU_SEQLENS 1u        /* cu_seqlens not non-decreasing within [0, T] */
@@ -193,6 +200,22 @@ int gdn_prefill(const gdn_prefill_params *p, void *stream);
  * computation is exactly that of gdn_prefill().  events is a host array. */
 int gdn_prefill_timed(const gdn_prefill_params *p, void *stream,
                       void *const events[5]);
+
+/* gdn_prefill() for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * workspace is a file-scope static device array of GDN_NOALLOC_SCRATCH_BYTES
+ * (128 MiB) instead of p->workspace / p->workspace_bytes, which are ignored.
+ * The caller still passes every input and output.  Nothing is allocated: no
+ * hipMalloc, no hipFree, no allocating library call.  The first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress) and
+ * keeps its address.  Returns GDN_ERR_SCRATCH when
+ * gdn_prefill_workspace_size(p) exceeds GDN_NOALLOC_SCRATCH_BYTES (nothing
+ * is launched), otherwise exactly what gdn_prefill() returns, with the same
+ * results.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind; no part of it needs to start at zero (every call writes
+ * what it reads), but calls that overlap in time on one GPU (different
+ * streams, or different host threads without ordering) race on it. */
+int gdn_prefill_noalloc(const gdn_prefill_params *p, void *stream);
 
 /*
  * One decode step: one new token per sequence, applied to the state with the

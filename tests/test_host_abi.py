@@ -262,3 +262,20 @@ def test_workspace_argument_checked():
         api.workspace_tensor(torch.zeros(200, dtype=torch.uint8)[::2], "cpu", 64)
     with pytest.raises(ValueError):
         api.workspace_tensor(ws, "meta", 64)            # another device
+
+
+def test_noalloc_host_checks_without_a_device():
+    # gdn_prefill_noalloc refuses a NULL parameter block and a call whose
+    # workspace exceeds its static scratch before it touches the GPU
+    nat = _lib()
+    L = nat.lib()
+    assert L.gdn_prefill_noalloc(None, None) == nat.ERR_CODE["GDN_ERR_NULL"]
+    p = nat.Params()
+    p.total_tokens, p.num_seqs = 1 << 20, 1
+    p.num_q_heads = p.num_k_heads = p.num_v_heads = 16
+    p.head_size = 128
+    p.qkv_dtype = 1
+    assert L.gdn_prefill_workspace_size(ctypes.byref(p)) > nat.NOALLOC_SCRATCH_BYTES
+    assert L.gdn_prefill_noalloc(ctypes.byref(p), None) == nat.ERR_CODE["GDN_ERR_SCRATCH"]
+    p.head_size = 48
+    assert L.gdn_prefill_noalloc(ctypes.byref(p), None) == nat.ERR_CODE["GDN_ERR_SHAPE"]
