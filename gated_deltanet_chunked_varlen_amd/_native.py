@@ -8,7 +8,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgdn_prefill.so")
+# GDN_PREFILL_LIB names another build of the library (e.g. one whose host
+# code carries sanitizers); the default is the in-tree build
+LIB_PATH = os.environ.get("GDN_PREFILL_LIB") or os.path.join(HERE, "libgdn_prefill.so")
 
 GDN_F32, GDN_BF16, GDN_F16, GDN_FP8_E4M3, GDN_FP8_E5M2 = 0, 1, 2, 3, 4
 GDN_I32, GDN_I64 = 0, 1

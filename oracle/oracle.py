@@ -44,19 +44,23 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build of gdn_oracle.c to load (e.g. one built with
+# sanitizers); it is loaded as it is, never rebuilt
+_LIB_OVERRIDE = os.environ.get("ORACLE_LIB")
 
 
-def build(force: bool = True) -> str:
-    """Compile ``gdn_oracle.c`` into ``liboracle.so`` with gcc (OpenMP)."""
-    if force or not os.path.exists(_LIB) or (
-            os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+def build(force: bool = True, out: str = _LIB, cc: str = "gcc", extra_flags=()) -> str:
+    """Compile ``gdn_oracle.c`` into ``liboracle.so`` (or ``out``) with gcc
+    and OpenMP; ``cc`` and ``extra_flags`` serve instrumented builds."""
+    if force or not os.path.exists(out) or (
+            os.path.getmtime(out) < os.path.getmtime(_SRC)):
+        tmp = out + ".tmp%d" % os.getpid()
         subprocess.check_call([
-            "gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
-            "-Wall", "-Wextra", "-Wno-unused-parameter", _SRC, "-o", tmp,
-            "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+            cc, "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+            "-Wall", "-Wextra", "-Wno-unused-parameter"] + list(extra_flags) + [
+            _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 class _Problem(ctypes.Structure):
@@ -92,10 +96,13 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or (
-                os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
-            build(force=True)
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or (
+                    os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+                build(force=True)
+            L = ctypes.CDLL(_LIB)
         L.oracle_chunk_table.restype = ctypes.c_int64
         L.oracle_chunk_table.argtypes = [
             ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
