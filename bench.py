@@ -479,7 +479,7 @@ def bench_decode(args):
     print(json.dumps(res), flush=True)
 
 
-def measure_prefill(wl, steps, warmup, cold_calls):
+def measure_prefill(wl, steps, warmup, cold_calls, use_cp="auto"):
     """Time one prefill workload: throughput over exactly ``steps`` calls after
     ``warmup`` untimed ones, per-phase times, the dominant kernel timed with
     HIP events on the call's stream, optionally cold-cache calls.  Returns a
@@ -504,7 +504,7 @@ def measure_prefill(wl, steps, warmup, cold_calls):
         kw.update(state_checkpoints=torch.empty((rows, H, D, D), device="cuda"),
                   checkpoint_cu_starts=d["checkpoint_cu_starts"],
                   checkpoint_every_n_tokens=wl.checkpoint_every)
-    p, out, outst = api.make_params(d["q"], d["k"], d["v"], **kw)
+    p, out, outst = api.make_params(d["q"], d["k"], d["v"], use_cp=use_cp, **kw)
     need = api.workspace_size(p)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     p.workspace, p.workspace_bytes = ctypes.c_void_p(ws.data_ptr()), need
@@ -727,6 +727,22 @@ def main():
     }
     res.update({k: v for k, v in r.items() if k not in ("ms_per_step", "tokens_per_s")})
     if args.workload == DEFAULT_WORKLOAD and not args.no_extra:
+        # context parallelism: one 65 536-token sequence with 4 heads, the
+        # ordinary pass against the context-parallel one ("auto" takes it)
+        wc = W.WORKLOADS["long65536h4"]()
+        k_cp = max(1, min(args.steps, 50))
+        m_off = measure_prefill(wc, k_cp, min(args.warmup, 50), 0, use_cp=False)
+        m_cp = measure_prefill(wc, k_cp, min(args.warmup, 50), 0, use_cp="auto")
+        ms_off, ms_cp = m_off["ms_total"] / m_off["K"], m_cp["ms_total"] / m_cp["K"]
+        res["context_parallel_1x65536_h4"] = {
+            "workload": wc.name, "steps": k_cp,
+            "ms_per_step_cp": ms_cp, "ms_per_step_no_cp": ms_off,
+            "speedup": ms_off / ms_cp,
+            "tokens_per_s_cp": wc.T / (ms_cp * 1e-3),
+            "phase_ms_warmup_cp": m_cp["phase_ms"],
+            "note": "the state phase holds the segment transitions, the start-state "
+                    "fix-up and the fused pass over all segments"}
+
         # the 2 x 2048-token, 16-head batch, timed the same way in this run
         w2 = W.WORKLOADS["varlen2x2048"]()
         r2 = prefill_record(measure_prefill(w2, args.steps, min(args.warmup, 500), 0))

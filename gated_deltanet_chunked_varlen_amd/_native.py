@@ -21,9 +21,11 @@ ERRORS = {
     -4: "GDN_ERR_DTYPE", -5: "GDN_ERR_CHECKPOINT", -6: "GDN_ERR_STATE",
     -7: "GDN_ERR_MAX_SEQLEN", -8: "GDN_ERR_WORKSPACE", -9: "GDN_ERR_STRIDES",
     -10: "GDN_ERR_DEVICE", -11: "GDN_ERR_LAUNCH", -12: "GDN_ERR_ALIGN",
-    -13: "GDN_ERR_SCRATCH",
+    -13: "GDN_ERR_SCRATCH", -14: "GDN_ERR_CP",
 }
 NOALLOC_SCRATCH_BYTES = 128 << 20
+CP_AUTO, CP_ON, CP_OFF = 0, 1, 2
+ABI_VERSION = 2
 ERR_CODE = {v: k for k, v in ERRORS.items()}
 STATUS_CU_SEQLENS = 1
 STATUS_CHECKPOINT_STARTS = 2
@@ -81,6 +83,8 @@ class Params(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("status", ctypes.c_void_p),
+        ("use_cp", ctypes.c_int32),
+        ("cp_chunk_len", ctypes.c_int64),
     ]
 
 
@@ -98,6 +102,9 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.gdn_abi_version.restype = ctypes.c_int
         L.gdn_abi_version.argtypes = []
+        if L.gdn_abi_version() != ABI_VERSION:
+            raise ImportError("libgdn_prefill.so has ABI version %d, this binding expects %d; "
+                              "rebuild it" % (L.gdn_abi_version(), ABI_VERSION))
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_max_chunks.restype = ctypes.c_int64

@@ -33,7 +33,7 @@ _INDEX_TYPES = {torch.int32: nat.GDN_I32, torch.int64: nat.GDN_I64}
 _VALUE_ERRORS = {"GDN_ERR_NULL", "GDN_ERR_SHAPE", "GDN_ERR_HEAD_RATIO",
                  "GDN_ERR_DTYPE", "GDN_ERR_CHECKPOINT", "GDN_ERR_STATE",
                  "GDN_ERR_MAX_SEQLEN", "GDN_ERR_WORKSPACE", "GDN_ERR_STRIDES",
-                 "GDN_ERR_ALIGN"}
+                 "GDN_ERR_ALIGN", "GDN_ERR_CP", "GDN_ERR_SCRATCH"}
 
 
 def _raise(rc: int):
@@ -93,10 +93,13 @@ def make_params(q, k, v, g=None, beta=None, scale=None, initial_state=None,
                 use_qk_l2norm_in_kernel=False, output=None, output_state=None,
                 state_checkpoints=None, checkpoint_cu_starts=None,
                 checkpoint_every_n_tokens=0, state_indices=None,
-                max_seqlen=None, status=None, decode=False):
+                max_seqlen=None, status=None, decode=False, use_cp="auto",
+                _cp_chunk_len=None):
     """Fill the C parameter block (allocates output / final state when the
     caller passes none).  Returns (params, output, output_state).  With
-    ``decode`` token i is sequence i's one new token (num_seqs = T)."""
+    ``decode`` token i is sequence i's one new token (num_seqs = T).
+    ``use_cp``: "auto", True or False (context parallelism within the GPU);
+    ``_cp_chunk_len``: its segment length in tokens, a multiple of 64."""
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors")
     dev = q.device
@@ -198,6 +201,13 @@ def make_params(q, k, v, g=None, beta=None, scale=None, initial_state=None,
         p.checkpoint_cu_starts_type = _index("checkpoint_cu_starts", checkpoint_cu_starts)
         p.checkpoint_cu_starts = _ptr(checkpoint_cu_starts)
     p.max_seqlen = 0 if max_seqlen is None else int(max_seqlen)
+    if isinstance(use_cp, str):
+        if use_cp != "auto":
+            raise ValueError('use_cp must be "auto", True or False')
+        p.use_cp = nat.CP_AUTO
+    else:
+        p.use_cp = nat.CP_ON if use_cp else nat.CP_OFF
+    p.cp_chunk_len = 0 if _cp_chunk_len is None else int(_cp_chunk_len)
     if status is not None:
         if status.dtype != torch.int32 or status.numel() < 1:
             raise ValueError("status must be an int32 tensor")
@@ -263,7 +273,8 @@ def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None,
                            output=None, output_state=None,
                            state_checkpoints=None, checkpoint_cu_starts=None,
                            checkpoint_every_n_tokens=0, state_indices=None,
-                           max_seqlen=None, status=None, workspace=None):
+                           max_seqlen=None, status=None, workspace=None,
+                           use_cp="auto", _cp_chunk_len=None):
     """Varlen chunked Gated Delta Rule prefill on the current stream.
 
     Shapes: q [T, hq, D], k [T, hk, D], v [T, hv, D] (float32 or bfloat16);
@@ -271,14 +282,18 @@ def chunk_gated_delta_rule(q, k, v, g=None, beta=None, scale=None,
     states [N or pool, H, D(v), D(k)].  ``status`` (optional int32 device
     tensor) receives the device-side check bits.  ``workspace`` (optional
     uint8 device tensor) is used instead of the workspace cached for the
-    current (device, stream).
+    current (device, stream).  ``use_cp`` ("auto", True, False) and
+    ``_cp_chunk_len`` (tokens, a multiple of 64) control context parallelism
+    within the GPU (gitcode "FlashInfer GDN Prefill 完全指南", sections "API
+    全参数解析" and "Cake GDN CP 后端"); True outside its domain (bf16 / fp16
+    inputs, head size 128, at most 63 sequences) raises.
     """
     lib = nat.lib()
     p, output, output_state = make_params(
         q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
         use_qk_l2norm_in_kernel, output, output_state, state_checkpoints,
         checkpoint_cu_starts, checkpoint_every_n_tokens, state_indices,
-        max_seqlen, status)
+        max_seqlen, status, use_cp=use_cp, _cp_chunk_len=_cp_chunk_len)
     need = int(lib.gdn_prefill_workspace_size(ctypes.byref(p)))
     if need == 0:
         rc = lib.gdn_validate_host(ctypes.byref(p))
@@ -309,7 +324,8 @@ def chunk_gated_delta_rule_noalloc(q, k, v, g=None, beta=None, scale=None,
                                    output=None, output_state=None,
                                    state_checkpoints=None, checkpoint_cu_starts=None,
                                    checkpoint_every_n_tokens=0, state_indices=None,
-                                   max_seqlen=None, status=None):
+                                   max_seqlen=None, status=None, use_cp="auto",
+                                   _cp_chunk_len=None):
     """``chunk_gated_delta_rule`` through gdn_prefill_noalloc: the library's
     static device scratch (128 MiB per GPU) serves as the workspace and
     nothing is allocated, here or in the library.  ``output`` (and
@@ -327,7 +343,7 @@ def chunk_gated_delta_rule_noalloc(q, k, v, g=None, beta=None, scale=None,
         q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
         use_qk_l2norm_in_kernel, output, output_state, state_checkpoints,
         checkpoint_cu_starts, checkpoint_every_n_tokens, state_indices,
-        max_seqlen, status)
+        max_seqlen, status, use_cp=use_cp, _cp_chunk_len=_cp_chunk_len)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = lib.gdn_prefill_noalloc(ctypes.byref(p), ctypes.c_void_p(stream))

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn_prefill.so")
 SOURCES = ["gdn_host.hip", "k0_chunk_index.hip", "k1_intra.hip",
-           "k2_state.hip", "k3_output.hip", "k4_decode.hip"]
+           "k2_state.hip", "k3_output.hip", "k4_decode.hip", "k5_cp.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -36,9 +36,61 @@ bool valid_state_dtype(int d) {
 }
 bool valid_itype(int t) { return t == GDN_I32 || t == GDN_I64; }
 
+// Context-parallel configuration of a call: segments of seg chunks, at most
+// nseg per sequence (0, 0: the ordinary pass).  Decided from the parameter
+// block alone (no device query: every gfx950 part has 256 compute units), so
+// the workspace size is known before a device is touched.
+constexpr int kCpCUs = 256;
+constexpr int64_t kCpMinSegChunks = 16;
+constexpr int64_t kCpMaxSegs = 4096;
+
+bool cp_domain(const gdn_prefill_params *p) {
+  return p->qkv_dtype != GDN_F32 && p->head_size == 128 && p->num_seqs >= 1 &&
+         p->num_seqs <= kDirectSeqs && p->total_tokens > 0;
+}
+
+struct CpConfig {
+  int32_t seg = 0, nseg = 0;
+};
+
+// Segment length: the batch's chunks over enough segments for two
+// 16-column tiles per compute unit in the final pass (its two-tile form),
+// and no shorter than kCpMinSegChunks chunks (the start-state fix-up is
+// serial over a sequence's segments).  Measured on the MI355X with one to
+// sixteen heads and 16 384 to 131 072 tokens per call: the best of segments
+// of 1 024 ... 16 384 tokens sits at this choice or within 4 % of it.  Auto
+// takes the context-parallel form when the ordinary pass occupies at most
+// half of the compute units and the longest possible sequence spans two or
+// more segments.
+CpConfig cp_config(const gdn_prefill_params *p) {
+  CpConfig c;
+  if (p->use_cp == GDN_CP_OFF || !cp_domain(p)) return c;
+  const int64_t maxlen = p->max_seqlen > 0 ? p->max_seqlen : p->total_tokens;
+  const int64_t maxc = (maxlen + GDN_CHUNK - 1) / GDN_CHUNK;
+  const int64_t H = std::max(p->num_q_heads, p->num_v_heads);
+  const int64_t tiles = (int64_t)p->num_seqs * H * (p->head_size / 16);
+  int64_t seg;
+  if (p->cp_chunk_len > 0) {
+    seg = p->cp_chunk_len / GDN_CHUNK;
+  } else {
+    const int64_t chunks = gdn_max_chunks(p->total_tokens, p->num_seqs);
+    const int64_t target = 2 * kCpCUs;  // tiles of the final pass
+    seg = std::max<int64_t>(kCpMinSegChunks, (chunks * H * (p->head_size / 16) + target - 1) / target);
+  }
+  seg = std::max<int64_t>(seg, 1);
+  if (p->use_cp == GDN_CP_AUTO && (tiles > kCpCUs / 2 || maxc < 2 * seg)) return c;
+  // bound the segment count (the grid), lengthening segments if needed
+  if ((maxc + seg - 1) / seg > kCpMaxSegs) seg = (maxc + kCpMaxSegs - 1) / kCpMaxSegs;
+  c.seg = (int32_t)std::min<int64_t>(seg, INT32_MAX);
+  c.nseg = (int32_t)std::max<int64_t>(1, (maxc + seg - 1) / seg);
+  return c;
+}
+
 struct Layout {
-  size_t chunk_idx, chunk_tok, cu_chunks, seq_bos, n_chunks, Wf, Kf, Uf, Hf, Nf, Qf, Pf, Gw, total;
+  size_t chunk_idx, chunk_tok, cu_chunks, seq_bos, n_chunks, Wf, Kf, Uf, Hf, Nf, Qf, Pf, Gw;
+  size_t cp_start, cp_sloc, cp_m, total;
   bool fuse;
+  CpConfig cp;
 };
 
 Layout plan(const gdn_prefill_params *p) {
@@ -68,6 +120,15 @@ Layout plan(const gdn_prefill_params *p) {
     L.Hf = take(blocks * D * D * es);
   }
   L.Gw = take(blocks * 64 * sizeof(float));
+  L.cp = cp_config(p);
+  if (L.cp.nseg > 0) {
+    // fp32 [N][nseg][H][D][D] each: segment start states, and each segment's
+    // state from a zero start and its transition matrix
+    const size_t st = (size_t)N * L.cp.nseg * H * D * D * sizeof(float);
+    L.cp_start = take(st);
+    L.cp_sloc = take(st);
+    L.cp_m = take(st);
+  }
   L.total = off;
   return L;
 }
@@ -152,6 +213,7 @@ const char *gdn_status_string(int code) {
     case GDN_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
     case GDN_ERR_LAUNCH: return "kernel launch failed";
     case GDN_ERR_ALIGN: return "q, k, v and output must be 16-byte aligned and the workspace 256-byte aligned";
+    case GDN_ERR_CP: return "use_cp must be 0 (auto), 1 (on) or 2 (off) and cp_chunk_len a non-negative multiple of 64; use_cp = on needs bf16 or fp16 inputs, head size 128 and at most 63 sequences";
     case GDN_ERR_SCRATCH: return "gdn_prefill_noalloc: the call needs more workspace than the static scratch (GDN_NOALLOC_SCRATCH_BYTES) or its address is unavailable";
     case (int)GDN_STATUS_CU_SEQLENS: return "status: cu_seqlens not non-decreasing within [0, total_tokens]";
     case (int)GDN_STATUS_CHECKPOINT_STARTS: return "status: checkpoint_cu_starts differs from the prefix sum of floor(len / n)";
@@ -224,6 +286,10 @@ int gdn_validate_host(const gdn_prefill_params *p) {
     const int64_t lo = (T + N - 1) / N;
     if (p->max_seqlen < lo || p->max_seqlen > T) return GDN_ERR_MAX_SEQLEN;
   }
+  // context parallelism
+  if (p->use_cp < GDN_CP_AUTO || p->use_cp > GDN_CP_OFF) return GDN_ERR_CP;
+  if (p->cp_chunk_len < 0 || p->cp_chunk_len % GDN_CHUNK != 0) return GDN_ERR_CP;
+  if (p->use_cp == GDN_CP_ON && !cp_domain(p) && T > 0) return GDN_ERR_CP;
   // workspace
   const size_t need = plan(p).total;
   if (p->workspace_bytes < need || (need > 0 && !p->workspace)) return GDN_ERR_WORKSPACE;
@@ -302,6 +368,13 @@ static void fill_args(const gdn_prefill_params *p, const Layout *L, int num_cus,
       a.Nf = ws + L->Nf;
     }
     a.Gw = (float *)(ws + L->Gw);
+    if (L->cp.nseg > 0) {
+      a.cp_seg = L->cp.seg;
+      a.cp_nseg = L->cp.nseg;
+      a.cp_start = (float *)(ws + L->cp_start);
+      a.cp_sloc = (float *)(ws + L->cp_sloc);
+      a.cp_m = (float *)(ws + L->cp_m);
+    }
   }
   a.cap = gdn_max_chunks(p->total_tokens, p->num_seqs);
   const int64_t rows = p->state_indices ? p->pool_size : p->num_seqs;
@@ -358,7 +431,14 @@ static int prefill_impl(const gdn_prefill_params *p, void *stream, void *const *
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess && a.cap > 0) e = launch_intra(a, s);
   if (e == hipSuccess) e = mark(2);
-  if (a.fuse) {
+  if (a.fuse && a.cp_nseg > 0) {
+    // context parallel: segment transitions, serial fix-up of the segment
+    // start states, then the fused pass over every segment
+    if (e == hipSuccess) e = launch_cp_transition(a, s);
+    if (e == hipSuccess) e = launch_cp_fixup(a, s);
+    if (e == hipSuccess) e = launch_state_output(a, s);
+    if (e == hipSuccess) e = mark(3);
+  } else if (a.fuse) {
     // state and output in one pass; the output phase is empty
     if (e == hipSuccess) e = launch_state_output(a, s);
     if (e == hipSuccess) e = mark(3);

@@ -88,6 +88,12 @@ struct Args {
   // one wave pulls into L2 (0: off; set when the intermediates outgrow the
   // last-level cache and the pass would read them from HBM)
   int32_t warm;
+  // context parallelism (16-bit inputs, direct mode): each sequence splits
+  // into segments of cp_seg chunks, at most cp_nseg of them; fp32
+  // [N][cp_nseg][H][D][D] buffers hold each segment's start state, its state
+  // from a zero start and its transition (row m = the transition's column m)
+  int32_t cp_seg, cp_nseg;
+  float *cp_start, *cp_sloc, *cp_m;
   // 16-bit intra-chunk pass, set with warm: write the intermediates with
   // non-temporal stores.  They then outgrow the last-level cache and are read
   // back from HBM anyway; below that size plain stores leave them in the
@@ -212,5 +218,7 @@ hipError_t launch_state(const Args &a, hipStream_t s);
 hipError_t launch_output(const Args &a, hipStream_t s);
 hipError_t launch_decode(const Args &a, hipStream_t s);
 hipError_t launch_state_output(const Args &a, hipStream_t s);
+hipError_t launch_cp_transition(const Args &a, hipStream_t s);
+hipError_t launch_cp_fixup(const Args &a, hipStream_t s);
 
 }  // namespace gdn

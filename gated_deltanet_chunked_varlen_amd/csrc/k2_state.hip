@@ -27,227 +27,10 @@
 // and share one XCD's L2 for the W / Ktilde blocks they all read.
 #include "gdn_common.h"
 #include "gdn_internal.h"
+#include "gdn_state.h"
 #include "../../include/gdn_prefill.h"
 
 namespace gdn {
-
-__device__ __forceinline__ int64_t ld_index(const void *p, int type, int64_t i) {
-  return type == GDN_I64 ? ((const int64_t *)p)[i] : (int64_t)((const int32_t *)p)[i];
-}
-
-// Operands of one chunk for one 16-column tile, as loaded by one lane.
-template <typename T, int D>
-struct ChunkOps {
-  typedef typename Mfma<T>::frag frag;
-  static constexpr int NT = Geo<T, D>::NT, KS_D = Geo<T, D>::KS_D, KS_C = Geo<T, D>::KS_C;
-  frag w[4][KS_D];     // W rows (4 tiles), contraction over dk
-  frag k[NT][KS_C];    // Ktilde^T rows (NT tiles), contraction over t
-  T u[4][4];           // U in result layout
-  float glog;          // G at the chunk's last row
-
-  __device__ __forceinline__ void load(const Args &a, int64_t ch, int jv, int lane) {
-    constexpr int KPL = Mfma<T>::KPL;
-    const T *wf = (const T *)a.Wf + ch * Geo<T, D>::W_ELEMS;
-    const T *kf = (const T *)a.Kf + ch * Geo<T, D>::W_ELEMS;
-    const T *uf = (const T *)a.Uf + ch * Geo<T, D>::W_ELEMS + (int64_t)jv * 4 * 64 * 4;
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-#pragma unroll
-      for (int kt = 0; kt < KS_D; ++kt)
-        w[it][kt] = *reinterpret_cast<const frag *>(wf + (((int64_t)it * KS_D + kt) * 64 + lane) * KPL);
-#pragma unroll
-    for (int it = 0; it < NT; ++it)
-#pragma unroll
-      for (int kt = 0; kt < KS_C; ++kt)
-        k[it][kt] = *reinterpret_cast<const frag *>(kf + (((int64_t)it * KS_C + kt) * 64 + lane) * KPL);
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) u[it][r] = uf[((int64_t)it * 64 + lane) * 4 + r];
-    glog = a.Gw[ch * kChunk + (kChunk - 1)];
-  }
-};
-
-// Operands held in registers (ChunkOps) ...
-template <typename T, int D>
-struct RegOps {
-  static constexpr bool kInterleave = false;
-  const ChunkOps<T, D> &op;
-  __device__ __forceinline__ typename Mfma<T>::frag w(int it, int kt) const { return op.w[it][kt]; }
-  __device__ __forceinline__ typename Mfma<T>::frag k(int it, int kt) const { return op.k[it][kt]; }
-  __device__ __forceinline__ f32x4 uvec(int it) const {
-    return f32x4{to_f32(op.u[it][0]), to_f32(op.u[it][1]), to_f32(op.u[it][2]), to_f32(op.u[it][3])};
-  }
-  __device__ __forceinline__ float glog() const { return op.glog; }
-};
-
-// One chunk of the state recurrence for one lane's share of a 16-column tile.
-// With xb non-null (the fused state/output pass) the chunk-start state and
-// N fragments go to that LDS buffer instead of the workspace: KS_D state
-// fragments, then KS_C new-value fragments, 64 lanes each.
-template <typename T, int D, typename Ops>
-__device__ __forceinline__ void chunk_step(const Args &a, const Ops &op,
-                                           float (&S)[D / 16][4], int64_t ch, int jv,
-                                           int lane,
-                                           typename Mfma<T>::frag *xb = nullptr) {
-  using M = Mfma<T>;
-  using Ge = Geo<T, D>;
-  typedef typename M::frag frag;
-  constexpr int KPL = Ge::KPL, NT = Ge::NT, KS_D = Ge::KS_D, KS_C = Ge::KS_C;
-  // The W fragments are read up front, so their reads are in flight together
-  // instead of one ahead of each product; the Ktilde fragments are read
-  // while the first product runs (one read per product issued).
-  frag wv[4][KS_D], kv[NT][KS_C];
-#pragma unroll
-  for (int kt = 0; kt < KS_D; ++kt)
-#pragma unroll
-    for (int it = 0; it < 4; ++it) wv[it][kt] = op.w(it, kt);
-  f32x4 acc[4];
-#pragma unroll
-  for (int it = 0; it < 4; ++it) acc[it] = op.uvec(it);
-  const float gl = gexp(op.glog());
-  __builtin_amdgcn_sched_barrier(0);
-  // the state as operand fragments (dk in pi order): slot s is S[s / 4][s % 4]
-  const float *Sflat = &S[0][0];
-  frag sb[KS_D];
-#pragma unroll
-  for (int kt = 0; kt < KS_D; ++kt) sb[kt] = M::pack(Sflat + kt * KPL);
-  // chunk-start state, stored for the output pass
-  if (xb) {
-#pragma unroll
-    for (int kt = 0; kt < KS_D; ++kt) xb[kt * 64 + lane] = sb[kt];
-  } else {
-    T *hf = (T *)a.Hf + ch * Ge::H_ELEMS + (int64_t)jv * KS_D * 64 * KPL;
-#pragma unroll
-    for (int kt = 0; kt < KS_D; ++kt)
-      *reinterpret_cast<frag *>(hf + ((int64_t)kt * 64 + lane) * KPL) = sb[kt];
-  }
-  // N = U + (-W) S      (the workspace holds -W)
-  float accf[16];
-  {
-#pragma unroll
-    for (int kt = 0; kt < KS_D; ++kt)
-#pragma unroll
-      for (int it = 0; it < 4; ++it) acc[it] = M::mma(wv[it][kt], sb[kt], acc[it]);
-#pragma unroll
-    for (int it = 0; it < NT; ++it)
-#pragma unroll
-      for (int kt = 0; kt < KS_C; ++kt) kv[it][kt] = op.k(it, kt);
-    if (Ops::kInterleave) {
-      // pair each product of the first GEMM with one Ktilde read
-#pragma unroll
-      for (int i = 0; i < 4 * KS_D; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) accf[4 * it + r] = acc[it][r];
-  }
-  // new values as operand fragments (t in pi order), stored for the output pass
-  frag nf[KS_C];
-  {
-    T *nfp = (T *)a.Nf + ch * Ge::W_ELEMS + (int64_t)jv * KS_C * 64 * KPL;
-#pragma unroll
-    for (int kt = 0; kt < KS_C; ++kt) {
-      nf[kt] = M::pack(accf + kt * KPL);
-      if (xb) xb[(KS_D + kt) * 64 + lane] = nf[kt];
-      else *reinterpret_cast<frag *>(nfp + ((int64_t)kt * 64 + lane) * KPL) = nf[kt];
-    }
-  }
-  // S' = exp(G_last) S + Ktilde^T N
-#pragma unroll
-  for (int it = 0; it < NT; ++it) {
-    f32x4 s4 = {S[it][0] * gl, S[it][1] * gl, S[it][2] * gl, S[it][3] * gl};
-#pragma unroll
-    for (int kt = 0; kt < KS_C; ++kt) s4 = M::mma(kv[it][kt], nf[kt], s4);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) S[it][r] = s4[r];
-  }
-}
-
-// A lane holds S[16 it + 4 g + r][vcol], r = 0..3: four consecutive k of
-// row vcol of the stored [V, K] state.  With unit k stride and every such
-// run aligned to its size (checked per call), each run moves as one vector
-// access (16 bytes in fp32, 8 in 16 bits); otherwise element by element.
-template <typename St>
-__device__ __forceinline__ bool state_runs_aligned(const void *p, const int64_t str[4]) {
-  constexpr int A = 4 * (int)sizeof(St);
-  return str[3] == 1 && (uintptr_t)p % A == 0 && (str[0] * (int64_t)sizeof(St)) % A == 0 &&
-         (str[1] * (int64_t)sizeof(St)) % A == 0 && (str[2] * (int64_t)sizeof(St)) % A == 0;
-}
-
-template <typename St, int D>
-__device__ __forceinline__ void write_state_t(St *p, const int64_t str[4], int64_t row, int h,
-                                              int vcol, int g, const float (&S)[D / 16][4]) {
-  const int64_t base = row * str[0] + (int64_t)h * str[1] + (int64_t)vcol * str[2];
-  if (state_runs_aligned<St>(p, str)) {
-#pragma unroll
-    for (int it = 0; it < D / 16; ++it) {
-      St x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = from_f32<St>(S[it][r]);
-      __builtin_memcpy(__builtin_assume_aligned(p + base + 16 * it + 4 * g, 4 * sizeof(St)), x,
-                       sizeof(x));
-    }
-    return;
-  }
-#pragma unroll
-  for (int it = 0; it < D / 16; ++it)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[base + (int64_t)(16 * it + 4 * g + r) * str[3]] = from_f32<St>(S[it][r]);
-}
-
-template <typename T, int D>
-__device__ __forceinline__ void write_state(void *base_ptr, int dtype, const int64_t str[4],
-                                         int64_t row, int h, int vcol, int g,
-                                         const float (&S)[D / 16][4]) {
-  if (dtype == GDN_F32) write_state_t<float, D>((float *)base_ptr, str, row, h, vcol, g, S);
-  else if (dtype == GDN_BF16) write_state_t<bf16, D>((bf16 *)base_ptr, str, row, h, vcol, g, S);
-  else if (dtype == GDN_F16) write_state_t<_Float16, D>((_Float16 *)base_ptr, str, row, h, vcol, g, S);
-  else if (dtype == GDN_FP8_E4M3) write_state_t<fp8e4m3, D>((fp8e4m3 *)base_ptr, str, row, h, vcol, g, S);
-  else write_state_t<fp8e5m2, D>((fp8e5m2 *)base_ptr, str, row, h, vcol, g, S);
-}
-
-template <typename St, int D>
-__device__ __forceinline__ void read_state_t(const St *p, const int64_t str[4], int64_t row, int h,
-                                             int vcol, int g, float (&S)[D / 16][4]) {
-  const int64_t base = row * str[0] + (int64_t)h * str[1] + (int64_t)vcol * str[2];
-  if (state_runs_aligned<St>(p, str)) {
-#pragma unroll
-    for (int it = 0; it < D / 16; ++it) {
-      St x[4];
-      __builtin_memcpy(x, __builtin_assume_aligned(p + base + 16 * it + 4 * g, 4 * sizeof(St)),
-                       sizeof(x));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[it][r] = to_f32(x[r]);
-    }
-    return;
-  }
-#pragma unroll
-  for (int it = 0; it < D / 16; ++it)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) S[it][r] = to_f32(p[base + (int64_t)(16 * it + 4 * g + r) * str[3]]);
-}
-
-template <int D>
-__device__ __forceinline__ void read_state(const Args &a, bool row_ok, int64_t row, int h,
-                                           int vcol, int g, float (&S)[D / 16][4]) {
-  if (a.init && row_ok) {
-    if (a.init_dtype == GDN_F32) read_state_t<float, D>((const float *)a.init, a.init_str, row, h, vcol, g, S);
-    else if (a.init_dtype == GDN_BF16) read_state_t<bf16, D>((const bf16 *)a.init, a.init_str, row, h, vcol, g, S);
-    else if (a.init_dtype == GDN_F16) read_state_t<_Float16, D>((const _Float16 *)a.init, a.init_str, row, h, vcol, g, S);
-    else if (a.init_dtype == GDN_FP8_E4M3) read_state_t<fp8e4m3, D>((const fp8e4m3 *)a.init, a.init_str, row, h, vcol, g, S);
-    else read_state_t<fp8e5m2, D>((const fp8e5m2 *)a.init, a.init_str, row, h, vcol, g, S);
-  } else {
-#pragma unroll
-    for (int it = 0; it < D / 16; ++it)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[it][r] = 0.f;
-  }
-}
 
 // Operands are double-buffered in registers where they fit (bf16, or fp32 up
 // to D = 64): the loads of chunk c+1 are issued before chunk c's products.
@@ -354,91 +137,6 @@ __global__ void __launch_bounds__(64) state_kernel(Args a) {
 // chunk st, the compute wave works on chunk st - 1, the output waves on
 // chunk st - 2 and start fetching chunk st.
 // ===========================================================================
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Direct loads into LDS: lane i's `bytes` bytes land at dst + bytes * i
-// (dst is the same for the whole wave).  Completion is counted by vmcnt.
-__device__ __forceinline__ void dma16(const void *src, unsigned char *dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void *src, unsigned char *dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 4, 0, 0);
-}
-
-// One LDS slot of the fused pass, laid out like the workspace blocks:
-// [W fragments][Ktilde fragments][the tile's U][gate row (64 floats)].
-// TW = 1 or 2 column tiles per workgroup: their U tiles sit side by side
-// (adjacent in the workspace too).
-template <typename T, int D, int TW = 1>
-struct DmaSlotGeo {
-  static constexpr int W_BYTES = 64 * D * (int)sizeof(T);
-  static constexpr int U_TILE_BYTES = 4 * 64 * 4 * (int)sizeof(T);   // 64 rows x 16 columns
-  static constexpr int K_OFF = W_BYTES, U_OFF = 2 * W_BYTES;
-  static constexpr int G_OFF = U_OFF + TW * U_TILE_BYTES;
-  static constexpr int BYTES = G_OFF + 64 * 4;
-  static constexpr int NV_W = W_BYTES / 1024;                         // 1 KB pieces per block
-  static constexpr int NP = 2 * NV_W + TW * U_TILE_BYTES / 1024;     // pieces (W, Ktilde, U)
-};
-
-template <typename T, int D, int TW = 1>
-struct DmaSlotOps {
-  static constexpr bool kInterleave = true;
-  typedef typename Mfma<T>::frag frag;
-  using SG = DmaSlotGeo<T, D, TW>;
-  static constexpr int KPL = Mfma<T>::KPL, KS_D = Geo<T, D>::KS_D, KS_C = Geo<T, D>::KS_C;
-  const unsigned char *slot;
-  int lane;
-  int utile;  // which of the slot's U tiles
-  __device__ __forceinline__ frag w(int it, int kt) const {
-    return *reinterpret_cast<const frag *>(slot + (((it * KS_D + kt) * 64 + lane) * KPL) * sizeof(T));
-  }
-  __device__ __forceinline__ frag k(int it, int kt) const {
-    return *reinterpret_cast<const frag *>(slot + SG::K_OFF + (((it * KS_C + kt) * 64 + lane) * KPL) * sizeof(T));
-  }
-  __device__ __forceinline__ f32x4 uvec(int it) const {
-    const T *up = reinterpret_cast<const T *>(slot + SG::U_OFF + utile * SG::U_TILE_BYTES) +
-                  (it * 64 + lane) * 4;
-    return f32x4{to_f32(up[0]), to_f32(up[1]), to_f32(up[2]), to_f32(up[3])};
-  }
-  __device__ __forceinline__ float glog() const {
-    return reinterpret_cast<const float *>(slot + SG::G_OFF)[kChunk - 1];
-  }
-};
-
-// Loader wave `part` of NLD: its share of a chunk's pieces (piece i goes to
-// part i % NLD; the gate row, one 4-byte-per-lane load, to the last part).
-template <typename T, int D, int NLD, int TW = 1>
-struct DmaLoader {
-  using SG = DmaSlotGeo<T, D, TW>;
-  static constexpr int NV_W = SG::NV_W;
-  static constexpr int64_t BLK = Geo<T, D>::W_ELEMS * sizeof(T) / 16;   // u32x4 per 64 x D block
-  static constexpr int NPC = SG::NP + 1;                                 // loads per chunk
-  static constexpr int PPW = (SG::NP + NLD - 1) / NLD;
-  // fewest loads any part issues per chunk: vmcnt thresholds built from it
-  // wait for at least the part's own older loads
-  static constexpr int MIN_PER_PART = NPC / NLD;
-  int64_t uoff;
-  int lane, part;
-
-  __device__ __forceinline__ void issue(const Args &a, int64_t ch, unsigned char *slot) const {
-    const u32x4 *wf = reinterpret_cast<const u32x4 *>(a.Wf) + ch * BLK + lane;
-    const u32x4 *kf = reinterpret_cast<const u32x4 *>(a.Kf) + ch * BLK + lane;
-    const u32x4 *uf = reinterpret_cast<const u32x4 *>(a.Uf) + ch * BLK + uoff + lane;
-#pragma unroll
-    for (int m = 0; m < PPW; ++m) {
-      const int i = part + NLD * m;
-      if (i < SG::NP) {
-        const u32x4 *src;
-        if (i < NV_W) src = wf + (int64_t)i * 64;
-        else if (i < 2 * NV_W) src = kf + (int64_t)(i - NV_W) * 64;
-        else src = uf + (int64_t)(i - 2 * NV_W) * 64;
-        dma16(src, slot + i * 1024);
-      }
-    }
-    if (part == NLD - 1) dma4(a.Gw + ch * kChunk + lane, slot + SG::G_OFF);
-  }
-};
-
 // L2 warm-up of a chunk ahead of the loaders and output waves: one 4-byte
 // load per 128-byte line of everything the chunk's workgroups will read,
 // sent into a junk LDS word (nothing waits on it).  The NT workgroups of a
@@ -482,12 +180,6 @@ struct L2Warm {
   }
 };
 
-// vmcnt(n) for the loader's waits (n <= 63).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
 
 // One output wave's operands for one chunk: q fragments of its two token
 // tiles, the unmasked P fragments (one for the first tile, two for the
@@ -619,7 +311,15 @@ template <> struct FusedRoles<2> {
 // operand traffic per column; it needs a three-slot ring (one chunk ahead
 // instead of two) to fit LDS, and is used when the one-tile grid does not fit
 // on the CUs at once, so that traffic, not the chain, bounds the pass.
-template <typename T, int D, int TW>
+//
+// CP: the context-parallel form (k5_cp.hip).  Workgroups cover (sequence,
+// segment, head) units instead of (sequence, head); a workgroup runs its
+// segment's chunks from the segment's start state in a.cp_start, writes the
+// checkpoints that fall inside the segment, and the final state only for the
+// segment that holds the sequence's last chunk.  Segments past a sequence's
+// end exit at once (segment 0 still runs for an empty sequence, whose final
+// state is its initial state).
+template <typename T, int D, int TW, bool CP = false>
 __global__ void __launch_bounds__(64 * FusedRoles<TW>::kWaves)
 state_output_kernel(Args a) {
   using R = FusedRoles<TW>;
@@ -641,14 +341,29 @@ state_output_kernel(Args a) {
   const int jg0 = jw * TW;             // first column tile
   const int u = (b / (8 * NWG)) * 8 + (b & 7);
   const int H = a.H;
-  if (u >= a.N * H) return;
+  const int NS = CP ? a.cp_nseg : 1;
+  if (u >= a.N * NS * H) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = u % H;
   const int g = lane >> 4, c = lane & 15;
 
   int f0, nc, len, sbos;
-  const int seq = seq_geometry_by_length(a, u / H, lane, f0, nc, len, sbos);
-  const int64_t ch0 = ws_index(f0, h, a.cap);
+  const int seq = seq_geometry_by_length(a, u / H / NS, lane, f0, nc, len, sbos);
+  // this workgroup's chunks: c0 .. c0 + nc - 1 of the sequence (all of them
+  // without CP); len and sbos become the segment's token count and first token
+  const int len_seq = len;
+  int c0 = 0, seg = 0;
+  bool last_seg = true;
+  if (CP) {
+    seg = (u / H) % NS;
+    c0 = seg * a.cp_seg;
+    if (seg > 0 && c0 >= nc) return;
+    last_seg = c0 + a.cp_seg >= nc;
+    nc = min(a.cp_seg, nc - c0);
+    len = min(len - kChunk * c0, kChunk * nc);
+    sbos += kChunk * c0;
+  }
+  const int64_t ch0 = ws_index(f0 + c0, h, a.cap);
 
   const bool hbm = a.warm > 0;
   const int ct = R::compute_tile(wave), ow = R::out_index(wave), part = R::loader_part(wave, hbm);
@@ -663,7 +378,12 @@ state_output_kernel(Args a) {
       row_ok = row >= 0 && row < a.pool_rows;
     }
     float S[NT][4];
-    read_state<D>(a, row_ok, row, h, vcol, g, S);
+    if (CP) {
+      const int64_t str[4] = {(int64_t)H * D * D, (int64_t)D * D, (int64_t)D, 1};
+      read_state_t<float, D>(a.cp_start, str, (int64_t)seq * NS + seg, h, vcol, g, S);
+    } else {
+      read_state<D>(a, row_ok, row, h, vcol, g, S);
+    }
     const int64_t ck_base = a.ck_every > 0 ? ld_index(a.ck_cs, a.ck_cs_type, seq) : 0;
     for (int st = 0; st <= nc + 1; ++st) {
       lds_sync();
@@ -672,15 +392,16 @@ state_output_kernel(Args a) {
       const DmaSlotOps<T, D, TW> op{cslots[cc % NSLOT], lane, ct};
       chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[ct][cc & 1]);
       if (a.ck_every > 0) {
-        const int done = (cc + 1) * kChunk;
-        if (done <= len && done % a.ck_every == 0) {
+        // tokens of the sequence done after this chunk
+        const int done = (c0 + cc + 1) * kChunk;
+        if (done <= len_seq && done % a.ck_every == 0) {
           const int64_t crow = ck_base + done / a.ck_every - 1;
           if (crow >= 0 && crow < a.ck_rows)
             write_state<T, D>(a.ck, a.ck_dtype, a.ck_str, crow, h, vcol, g, S);
         }
       }
     }
-    if (a.out_final && a.outst && row_ok)
+    if (last_seg && a.out_final && a.outst && row_ok)
       write_state<T, D>(a.outst, a.out_dtype, a.out_str, row, h, vcol, g, S);
   } else if (ow >= 0) {
     // ---------------- output waves ------------------------------------------
@@ -742,16 +463,26 @@ state_output_kernel(Args a) {
 template <typename T, int D, int TW>
 static hipError_t launch_state_output_tw(const Args &a, hipStream_t s) {
   constexpr int NWG = D / 16 / TW;
-  const int64_t units = (int64_t)a.N * a.H;
+  const bool cp = a.cp_nseg > 0;
+  const int64_t units = (int64_t)a.N * a.H * (cp ? a.cp_nseg : 1);
   const int64_t blocks = ((units + 7) / 8) * 8 * NWG;
-  state_output_kernel<T, D, TW><<<dim3((unsigned)blocks), dim3(64 * FusedRoles<TW>::kWaves), 0, s>>>(a);
+  const dim3 grid((unsigned)blocks), block(64 * FusedRoles<TW>::kWaves);
+  if constexpr (D == 128) {
+    if (cp) {
+      state_output_kernel<T, D, TW, true><<<grid, block, 0, s>>>(a);
+      return hipGetLastError();
+    }
+  } else {
+    if (cp) return hipErrorInvalidValue;
+  }
+  state_output_kernel<T, D, TW><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_state_output_t(const Args &a, hipStream_t s) {
   constexpr int NT = D / 16;
-  const int64_t units = (int64_t)a.N * a.H;
+  const int64_t units = (int64_t)a.N * a.H * (a.cp_nseg > 0 ? a.cp_nseg : 1);
   if (units == 0) return hipSuccess;
   // one workgroup per CU (LDS): two tiles per workgroup once the one-tile
   // grid no longer fits on the CUs at once (the GVA batch with 32 heads and 8

@@ -311,6 +311,15 @@ def long_l262144_h32_d128() -> Workload:
                 name="long_L262144_h32_d128_bf16")
 
 
+def long_l65536_h4_d128() -> Workload:
+    """One sequence of 65536 tokens (1024 chunks) with 4 heads, head size 128,
+    bf16, in-kernel q/k L2 norm, alpha ~ U[0.9, 1], fp32 initial and final
+    states: a long prompt with too few (sequence, head) pairs to fill the GPU,
+    the shape context parallelism is for."""
+    return make(1006, [65536], 4, 4, 4, 128, "bf16", l2norm_in_kernel=True,
+                init="seq", init_std=0.02, name="long_L65536_h4_d128_bf16")
+
+
 def decode_batch() -> Workload:
     """One decode step for 256 sequences (one new token each), 16 heads, head
     size 128, bf16, in-kernel q/k L2 norm, alpha ~ U[0.9, 1], fp32 512-slot
@@ -327,5 +336,6 @@ WORKLOADS = {
     "ragged6": ragged6_pool64_h16_d128,
     "gva8": gva8_h16x32_d128_checkpoints,
     "long262144": long_l262144_h32_d128,
+    "long65536h4": long_l65536_h4_d128,
     "decode": decode_batch,
 }

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 #define GDN_CHUNK 64 /* kernel chunk length in tokens */
 
 /* Element types.  The two 8-bit float types (OCP FP8 E4M3, max 448, and
@@ -69,6 +69,9 @@ typedef enum { GDN_I32 = 0, GDN_I64 = 1 } gdn_itype;
 #define GDN_ERR_ALIGN -12        /* q, k, v or output not 16-byte aligned, or the
                                     workspace not 256-byte aligned (the kernels
                                     move them in 16-byte vector accesses) */
+#define GDN_ERR_CP -14          /* use_cp outside {0, 1, 2}, cp_chunk_len not a
+                                    non-negative multiple of 64, or GDN_CP_ON
+                                    for a call outside the CP domain */
 #define GDN_ERR_SCRATCH -13      /* gdn_prefill_noalloc(): the call needs more
                                     workspace than GDN_NOALLOC_SCRATCH_BYTES, or
                                     the static scratch's address is unavailable */
@@ -151,7 +154,26 @@ typedef struct gdn_prefill_params {
   void *workspace;
   size_t workspace_bytes;
   int32_t *status;        /* optional device word */
+  /* Context parallelism within the GPU (gitcode, sections "API 全参数解析"
+   * (use_cp, _cp_chunk_len, max_seqlen) and "Cake GDN CP 后端" ("四阶段执行
+   * 流程"): each sequence is cut into segments of cp_chunk_len tokens, each
+   * segment's state transition is formed in parallel, the segment start
+   * states are fixed up serially, then every segment runs the ordinary pass
+   * from its start state.  use_cp: GDN_CP_AUTO (0) takes it when the call has
+   * too few (sequence, head) pairs to fill the GPU and long sequences;
+   * GDN_CP_ON (1) requires it and fails closed (GDN_ERR_CP) outside its
+   * domain (bf16 / fp16 inputs, head size 128, at most 63 sequences);
+   * GDN_CP_OFF (2) never takes it.  cp_chunk_len: 0 = chosen from the shape
+   * and max_seqlen (or total_tokens), else a positive multiple of 64 (for
+   * tests and tuning).  The results are those of the non-CP pass up to
+   * floating-point rounding. */
+  int32_t use_cp;
+  int64_t cp_chunk_len;
 } gdn_prefill_params;
+
+#define GDN_CP_AUTO 0
+#define GDN_CP_ON 1
+#define GDN_CP_OFF 2
 
 /* ABI version (GDN_ABI_VERSION). */
 int gdn_abi_version(void);

@@ -41,7 +41,7 @@ def test_header_symbols_exported():
 
 def test_abi_version_and_strings():
     nat = _lib()
-    assert nat.lib().gdn_abi_version() == 1
+    assert nat.lib().gdn_abi_version() == 2
     for code in list(nat.ERRORS) + [1, 2, 4, 8]:
         assert nat.status_string(code) != "unknown code"
 
@@ -279,3 +279,52 @@ def test_noalloc_host_checks_without_a_device():
     assert L.gdn_prefill_noalloc(ctypes.byref(p), None) == nat.ERR_CODE["GDN_ERR_SCRATCH"]
     p.head_size = 48
     assert L.gdn_prefill_noalloc(ctypes.byref(p), None) == nat.ERR_CODE["GDN_ERR_SHAPE"]
+
+
+def test_params_struct_layout_matches_the_header():
+    # the ctypes view against offsetof / sizeof from a C compiler reading
+    # include/gdn_prefill.h
+    import tempfile
+    nat = _lib()
+    fields = [f for f, _ in nat.Params._fields_]
+    src = ['#include <stdio.h>', '#include <stddef.h>',
+           '#include "%s"' % os.path.join(ROOT, "include", "gdn_prefill.h"),
+           "int main(void) {",
+           '  printf("%zu\\n", sizeof(gdn_prefill_params));']
+    src += ['  printf("%%zu\\n", offsetof(gdn_prefill_params, %s));' % f for f in fields]
+    src += ["  return 0;", "}"]
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write("\n".join(src))
+        subprocess.check_call(["gcc", "-std=c99", c, "-o", exe])
+        got = [int(x) for x in subprocess.check_output([exe]).split()]
+    assert got[0] == ctypes.sizeof(nat.Params)
+    assert got[1:] == [getattr(nat.Params, f).offset for f in fields]
+
+
+def test_context_parallel_arguments_checked():
+    nat = _lib()
+    L = nat.lib()
+    assert _validate(_params(T=8192, N=1, hq=2, hk=2, hv=2, cu=False,
+                             extra=dict(use_cp=nat.CP_ON))) == 0
+    assert _validate(_params(extra=dict(use_cp=3))) == code("GDN_ERR_CP")
+    assert _validate(_params(extra=dict(use_cp=-1))) == code("GDN_ERR_CP")
+    assert _validate(_params(extra=dict(cp_chunk_len=100))) == code("GDN_ERR_CP")
+    assert _validate(_params(extra=dict(cp_chunk_len=-64))) == code("GDN_ERR_CP")
+    # on, outside the domain: head size 64, fp32 inputs, more than 63 sequences
+    assert _validate(_params(D=64, extra=dict(use_cp=nat.CP_ON))) == code("GDN_ERR_CP")
+    assert _validate(_params(dtype=nat.GDN_F32, extra=dict(use_cp=nat.CP_ON))) == code("GDN_ERR_CP")
+    assert _validate(_params(T=6400, N=100, extra=dict(use_cp=nat.CP_ON))) == code("GDN_ERR_CP")
+    # auto, off and the segment length move the workspace: a long call with
+    # two heads takes CP under auto (fp32 start states, local states and
+    # transitions, [N][segments][H][D][D] each)
+    ws = lambda **e: L.gdn_prefill_workspace_size(ctypes.byref(
+        _params(T=16384, N=1, hq=2, hk=2, hv=2, cu=False, extra=e)))
+    base = ws(use_cp=nat.CP_OFF)
+    assert ws(use_cp=nat.CP_AUTO) > base
+    assert ws(use_cp=nat.CP_ON, cp_chunk_len=1024) == base + 3 * 16 * 2 * 128 * 128 * 4
+    # a batch that fills the GPU stays on the ordinary pass under auto
+    big = lambda **e: L.gdn_prefill_workspace_size(ctypes.byref(
+        _params(T=4096, N=2, hq=16, hk=16, hv=16, extra=e)))
+    assert big(use_cp=nat.CP_AUTO) == big(use_cp=nat.CP_OFF)
