@@ -152,12 +152,13 @@ struct L2Warm {
   static constexpr int SHARED = 3 * WL + PL;
   static constexpr int UL = TW * DmaSlotGeo<T, D>::U_TILE_BYTES / LINE;  // this workgroup's U
   static constexpr int GL = 64 * 4 / LINE;
-  static_assert(UL + GL <= 64, "one line per lane");
 
   // jw: this workgroup's index among the NWG of its (sequence, head); its
-  // tiles are TW jw .. TW jw + TW - 1
-  __device__ __forceinline__ static void touch(const Args &a, int64_t ch, int jw, int lane,
-                                               unsigned char *junk) {
+  // tiles are TW jw .. TW jw + TW - 1.  touch_shared: the workgroup's share
+  // of the lines all NWG workgroups read; touch_own: its U tiles and the
+  // gate row.
+  __device__ __forceinline__ static void touch_shared(const Args &a, int64_t ch, int jw, int lane,
+                                                      unsigned char *junk) {
     const unsigned char *wf = (const unsigned char *)a.Wf + ch * (WL * LINE);
     const unsigned char *kf = (const unsigned char *)a.Kf + ch * (WL * LINE);
     const unsigned char *qf = (const unsigned char *)a.Qf + ch * (WL * LINE);
@@ -172,11 +173,45 @@ struct L2Warm {
                                : pf + (lc - 3 * WL) * LINE;
       dma4(src, junk);
     }
+  }
+  __device__ __forceinline__ static void touch_own(const Args &a, int64_t ch, int jw, int lane,
+                                                   unsigned char *junk) {
     const unsigned char *uf = (const unsigned char *)a.Uf + ch * (WL * LINE) +
                               (int64_t)jw * TW * DmaSlotGeo<T, D>::U_TILE_BYTES;
     const unsigned char *gw = (const unsigned char *)(a.Gw + ch * kChunk);
-    const int l = min(lane, UL + GL - 1);
-    dma4(l < UL ? uf + l * LINE : gw + (l - UL) * LINE, junk);
+#pragma unroll
+    for (int l0 = 0; l0 < UL + GL; l0 += 64) {
+      const int l = min(l0 + lane, UL + GL - 1);
+      dma4(l < UL ? uf + l * LINE : gw + (l - UL) * LINE, junk);
+    }
+  }
+  __device__ __forceinline__ static void touch(const Args &a, int64_t ch, int jw, int lane,
+                                               unsigned char *junk) {
+    touch_shared(a, ch, jw, lane, junk);
+    touch_own(a, ch, jw, lane, junk);
+  }
+};
+
+// The compute wave's operands when its U tile comes through its own
+// registers (four-tile workgroups, whose LDS slots hold W and Ktilde only).
+template <typename T, int D>
+struct SlotRegUOps : DmaSlotOps<T, D, 0> {
+  const T (*u)[4];
+  __device__ __forceinline__ f32x4 uvec(int it) const {
+    return f32x4{to_f32(u[it][0]), to_f32(u[it][1]), to_f32(u[it][2]), to_f32(u[it][3])};
+  }
+};
+
+// One chunk's U tile for one lane of a compute wave (result layout, as in
+// ChunkOps::load).
+template <typename T, int D>
+struct UTile {
+  T u[4][4];
+  __device__ __forceinline__ void load(const Args &a, int64_t ch, int jv, int lane) {
+    const T *uf = (const T *)a.Uf + ch * Geo<T, D>::W_ELEMS + (int64_t)jv * 4 * 64 * 4;
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+      __builtin_memcpy(u[it], uf + ((int64_t)it * 64 + lane) * 4, sizeof(u[it]));
   }
 };
 
@@ -270,10 +305,18 @@ __device__ __forceinline__ void output_wave_step(const Args &a, int st, int nc, 
   lds_sync();
   into.issue(a, ch0 + (int64_t)min(st, nc - 1), lane, ow);
   const int oc = st - 2;
+  const int64_t tok0 = (int64_t)sbos + (int64_t)kChunk * oc;
+  const int rows = min(kChunk, len - kChunk * oc);
+  if constexpr (TW >= 4) {
+    // one tile at a time (keeps the wave's registers within its share)
+#pragma unroll 1
+    for (int t = 0; t < TW; ++t)
+      output_regs<T, D>(a, proc, xbuf[t][oc & 1], jg0 + t, tok0, rows, h, lane, ow);
+  } else {
 #pragma unroll
-  for (int t = 0; t < TW; ++t)
-    output_regs<T, D>(a, proc, xbuf[t][oc & 1], jg0 + t, (int64_t)sbos + (int64_t)kChunk * oc,
-                      min(kChunk, len - kChunk * oc), h, lane, ow);
+    for (int t = 0; t < TW; ++t)
+      output_regs<T, D>(a, proc, xbuf[t][oc & 1], jg0 + t, tok0, rows, h, lane, ow);
+  }
 }
 
 constexpr int kFusedLoadWaves = 2;
@@ -305,6 +348,18 @@ template <> struct FusedRoles<2> {
   __device__ static int warm_wave(bool) { return 5; }
   __device__ static int loader_part(int w, bool) { return w == 4 ? 0 : w == 6 ? 1 : -1; }
 };
+// TW = 4 (eight waves): compute waves 0-3 (one per tile and SIMD), output
+// waves 4 and 5 (each for all four tiles), loaders 6 and 7.  There is no L2
+// warm-up: the GVA batch (8 sequences, 32 heads, 868 MB of intermediates)
+// ran 0.480 ms per call without one against 0.524 ms with the output waves
+// touching the lines two chunks ahead.
+template <> struct FusedRoles<4> {
+  static constexpr int kWaves = 8, kSlots = 3;
+  __device__ static int compute_tile(int w) { return w < 4 ? w : -1; }
+  __device__ static int out_index(int w) { return w == 4 ? 0 : w == 5 ? 1 : -1; }
+  __device__ static int warm_wave(bool) { return -1; }
+  __device__ static int loader_part(int w, bool) { return w == 6 ? 0 : w == 7 ? 1 : -1; }
+};
 
 // TW column tiles per workgroup.  TW = 2 shares the workgroup's W / Ktilde
 // loads and its output waves' q / P loads between two tiles, which halves the
@@ -325,8 +380,12 @@ state_output_kernel(Args a) {
   using R = FusedRoles<TW>;
   constexpr int NT = D / 16, NWG = NT / TW, NLD = kFusedLoadWaves, NSLOT = R::kSlots;
   constexpr int AHEAD = NSLOT - 2;     // chunks the loaders run ahead
-  using SG = DmaSlotGeo<T, D, TW>;
-  using LD = DmaLoader<T, D, NLD, TW>;
+  // four tiles: the slots hold W, Ktilde and the gate row, and each compute
+  // wave fetches its U tile into registers (LDS holds three such slots and
+  // the four tiles' double-buffered hand-off)
+  constexpr bool UREG = TW >= 4;
+  using SG = DmaSlotGeo<T, D, UREG ? 0 : TW>;
+  using LD = DmaLoader<T, D, NLD, UREG ? 0 : TW>;
   typedef typename Mfma<T>::frag frag;
   constexpr int XB = Geo<T, D>::KS_D + Geo<T, D>::KS_C;  // fragments per chunk in xbuf
   static_assert(AHEAD == 1 || AHEAD == 2, "the loader waits below handle one or two chunks ahead");
@@ -385,12 +444,7 @@ state_output_kernel(Args a) {
       read_state<D>(a, row_ok, row, h, vcol, g, S);
     }
     const int64_t ck_base = a.ck_every > 0 ? ld_index(a.ck_cs, a.ck_cs_type, seq) : 0;
-    for (int st = 0; st <= nc + 1; ++st) {
-      lds_sync();
-      if (st == 0 || st > nc) continue;
-      const int cc = st - 1;
-      const DmaSlotOps<T, D, TW> op{cslots[cc % NSLOT], lane, ct};
-      chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[ct][cc & 1]);
+    auto checkpoint = [&](int cc) {
       if (a.ck_every > 0) {
         // tokens of the sequence done after this chunk
         const int done = (c0 + cc + 1) * kChunk;
@@ -399,6 +453,44 @@ state_output_kernel(Args a) {
           if (crow >= 0 && crow < a.ck_rows)
             write_state<T, D>(a.ck, a.ck_dtype, a.ck_str, crow, h, vcol, g, S);
         }
+      }
+    };
+    if constexpr (UREG) {
+      // U tiles in a two-deep register ring: step st works on chunk st - 1
+      // and fetches chunk st (the last chunk again at the end); whole rounds
+      // of the ring keep the compiler's waits exact
+      UTile<T, D> u0, u1;
+      auto cstep = [&](int st, const UTile<T, D> &use, UTile<T, D> &fill) {
+        fill.load(a, ch0 + (int64_t)min(st, nc - 1), jg, lane);
+        lds_sync();
+        const int cc = st - 1;
+        SlotRegUOps<T, D> op;
+        op.slot = cslots[cc % NSLOT];
+        op.lane = lane;
+        op.utile = 0;
+        op.u = use.u;
+        chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[ct][cc & 1]);
+        checkpoint(cc);
+      };
+      if (nc > 0) u0.load(a, ch0, jg, lane);
+      lds_sync();
+      if (nc > 0) {
+        int st = 1;
+        for (; st + 2 <= nc + 1; st += 2) {
+          cstep(st, u0, u1);
+          cstep(st + 1, u1, u0);
+        }
+        if (st <= nc) cstep(st, u0, u1);
+      }
+      lds_sync();
+    } else {
+      for (int st = 0; st <= nc + 1; ++st) {
+        lds_sync();
+        if (st == 0 || st > nc) continue;
+        const int cc = st - 1;
+        const DmaSlotOps<T, D, TW> op{cslots[cc % NSLOT], lane, ct};
+        chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[ct][cc & 1]);
+        checkpoint(cc);
       }
     }
     if (last_seg && a.out_final && a.outst && row_ok)
@@ -487,8 +579,14 @@ static hipError_t launch_state_output_t(const Args &a, hipStream_t s) {
   // one workgroup per CU (LDS): two tiles per workgroup once the one-tile
   // grid no longer fits on the CUs at once (the GVA batch with 32 heads and 8
   // sequences: 0.427 -> 0.317 ms); up to that the chain bounds the pass and
-  // one tile per workgroup spreads it over more CUs
-  if (units * NT > (int64_t)(a.num_cus > 0 ? a.num_cus : 1)) return launch_state_output_tw<T, D, 2>(a, s);
+  // one tile per workgroup spreads it over more CUs.  Four tiles once even
+  // the four-tile grid covers every CU: the operand traffic per column halves
+  // again.
+  const int64_t cus = a.num_cus > 0 ? a.num_cus : 1;
+  if constexpr (NT % 4 == 0) {
+    if (units * NT >= 4 * cus) return launch_state_output_tw<T, D, 4>(a, s);
+  }
+  if (units * NT > cus) return launch_state_output_tw<T, D, 2>(a, s);
   return launch_state_output_tw<T, D, 1>(a, s);
 }
 
