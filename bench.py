@@ -53,9 +53,12 @@ DEFAULT_WORKLOAD = "gva8"
 TRAFFIC_SOURCE = ("committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary (profiles/traffic.json), "
                   "taken on the same kernel source (hash-matched); not measured in this run")
 KERNEL_SOURCES = {
-    "chunk_index": "k0_chunk_index.hip", "intra": "k1_intra.hip",
-    "state": "k2_state.hip", "output": "k3_output.hip", "decode": "k4_decode.hip",
+    "chunk_index": ("k0_chunk_index.hip",), "intra": ("k1_intra.hip",),
+    "state": ("k2_state.hip", "k5_cp.hip"), "output": ("k3_output.hip",),
+    "decode": ("k4_decode.hip",),
 }
+# headers every kernel source includes
+COMMON_SOURCES = ("gdn_common.h", "gdn_internal.h", "gdn_state.h")
 
 
 def per_token_head_bytes(wl, phase):
@@ -174,11 +177,13 @@ def elapsed_ms(L, a, b):
     return float(ms.value)
 
 
-def source_hash(name):
-    path = os.path.join(ROOT, "gated_deltanet_chunked_varlen_amd", "csrc", name)
+def source_hash(names):
+    """Hash of a phase's kernel sources and the shared headers: counters taken
+    on other sources are not used."""
+    d = os.path.join(ROOT, "gated_deltanet_chunked_varlen_amd", "csrc")
     h = hashlib.sha256()
-    for p in (path, os.path.join(os.path.dirname(path), "gdn_common.h")):
-        with open(p, "rb") as f:
+    for n in tuple(names) + COMMON_SOURCES:
+        with open(os.path.join(d, n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -249,7 +254,8 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 
 
 PROF_KERNELS = {"chunk_index": ("chunk_index_kernel",), "intra": ("intra_kernel", "intra_kernel_h"),
-                "state": ("state_kernel", "state_output_kernel"),
+                "state": ("state_kernel", "state_output_kernel", "cp_transition_kernel",
+                          "cp_fixup_kernel"),
                 "output": ("output_kernel",), "decode": ("decode_kernel",)}
 
 
@@ -293,11 +299,13 @@ def _counters(d):
 
 
 def _by_phase(table):
+    """Per call and phase: each kernel's mean over its dispatches, summed over
+    the kernels of the phase (the context-parallel state phase runs three)."""
     res = {}
     for ph in PROF_KERNELS:
-        vals = [v for name, vs in table.items() if _phase_of(name) == ph for v in vs]
-        if vals:
-            res[ph] = sum(vals) / len(vals)
+        means = [sum(vs) / len(vs) for name, vs in table.items() if _phase_of(name) == ph and vs]
+        if means:
+            res[ph] = sum(means)
     return res
 
 
