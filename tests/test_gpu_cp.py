@@ -20,6 +20,7 @@ import pytest
 from gated_deltanet_chunked_varlen_amd import api, chunk_gated_delta_rule
 from gated_deltanet_chunked_varlen_amd import _native as nat
 from gated_deltanet_chunked_varlen_amd import workloads as W
+from oracle import oracle
 from tests import gdn_testlib as tl
 
 pytestmark = pytest.mark.gpu
@@ -114,7 +115,7 @@ def test_cp_on_outside_its_domain_fails_closed():
 def test_cp_long_l262144_h32_d128_sampled_heads():
     # the 262 144-token, 32-head call in eight segments of 32 768 tokens
     wl = W.long_l262144_h32_d128()
-    heads = [0, 31]
+    heads = [0, 13, 31]
     gpu = tl.run_gpu(wl, use_cp=True, _cp_chunk_len=32768)
     orc = tl.run_oracle(wl, heads=heads)
     _check(wl, gpu, orc, heads=heads)
@@ -126,3 +127,95 @@ def test_cp_auto_long_l65536_h4_bench_workload():
     gpu = tl.run_gpu(wl, status=True)
     assert gpu["status"] == 0
     _check(wl, gpu, tl.run_oracle(wl))
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+def cp_workspace_offsets(T, N, H, D, nseg):
+    """Byte offsets of the context-parallel buffers in a 16-bit call's
+    workspace (the layout of gdn_prefill_workspace_size: chunk tables, then
+    W, Ktilde, U, q fragments, P, gates, then the segment start states, local
+    states and transitions, each 256-byte aligned)."""
+    cap = int(nat.lib().gdn_max_chunks(T, N))
+    blocks = cap * H
+    sizes = [8 * max(cap, 1), 8 * max(cap, 1), 4 * (N + 1), 4 * (N + 1), 4,
+             blocks * 64 * D * 2, blocks * 64 * D * 2, blocks * 64 * D * 2,
+             blocks * 64 * D * 2, blocks * 64 * 64 * 2, blocks * 64 * 4]
+    off = 0
+    for sz in sizes:
+        off = _align(off + sz)
+    st = N * nseg * H * D * D * 4
+    start = off
+    sloc = _align(start + st)
+    mt = _align(sloc + st)
+    return start, sloc, mt, _align(mt + st)
+
+
+def _decode_m(block, D):
+    """The transition M[k][m] from its stored operand order."""
+    k = np.arange(D)[:, None]
+    m = np.arange(D)[None, :]
+    idx = (((k // 16) * (D // 16) + m // 16) * 64 + 16 * (m % 4) + k % 16) * 4 + (m // 4) % 4
+    return block[idx]
+
+
+def test_cp_segment_pairs_and_start_states_match_oracle():
+    # gitcode, "四阶段执行流程" (M/N precompute, state fix-up) and 0539edu
+    # section 2.1 (a run of chunks acts on its start state as an affine map):
+    # each non-final segment's local state is the segment run from zero,
+    # its transition M satisfies run(X) - run(0) = M X for any start X, and
+    # each segment start state is the prefix run from the initial state
+    lengths, H, D, seg = [1000, 300], 2, 128, 256
+    wl = W.make(126, lengths, H, H, H, D, "bf16", l2norm_in_kernel=True, init="seq",
+                init_std=0.3)
+    d = tl.to_device(wl)
+    N, T = wl.N, wl.T
+    nseg = -(-(-(-T // 64)) // (seg // 64))
+    start_off, sloc_off, m_off, end = cp_workspace_offsets(T, N, H, D, nseg)
+    p, _, _ = api.make_params(d["q"], d["k"], d["v"], cu_seqlens=d["cu_seqlens"],
+                              use_cp=True, _cp_chunk_len=seg)
+    assert api.workspace_size(p) == end
+    ws = torch.zeros(end, dtype=torch.uint8, device="cuda")
+    chunk_gated_delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=wl.scale,
+                           cu_seqlens=d["cu_seqlens"], use_qk_l2norm_in_kernel=True,
+                           initial_state=d["initial_state"], output_final_state=True,
+                           use_cp=True, _cp_chunk_len=seg, workspace=ws)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    blk = D * D * 4
+    f32 = lambda off, i, p_, h: raw[off + (((i * nseg + p_) * H + h) * blk):
+                                    off + (((i * nseg + p_) * H + h) * blk) + blk].view(np.float32)
+    rng = np.random.default_rng(7)
+    cu = wl.cu_seqlens.astype(np.int64)
+
+    def run(b, e, init):
+        prob = oracle.Problem(q=wl.q[b:e], k=wl.k[b:e], v=wl.v[b:e], cu=np.array([0, e - b]),
+                              g=wl.g[b:e], beta=wl.beta[b:e], scale=wl.scale, l2norm=True,
+                              init_state=init, state_indices=None, ckpt_every=0,
+                              ckpt_cu_starts=None)
+        return oracle.token(prob)["final"][0]            # [H, V, K]
+
+    checked = 0
+    for i in range(N):
+        b, e = int(cu[i]), int(cu[i + 1])
+        used = max(1, -(-(e - b) // seg))
+        for p_ in range(used):
+            sb = b + seg * p_
+            want_start = run(b, sb, wl.initial_state[i:i + 1]) if p_ > 0 else wl.initial_state[i]
+            got_start = np.stack([f32(start_off, i, p_, h).reshape(D, D) for h in range(H)])
+            assert tl.rel_l2(got_start, want_start) < 2e-2, (i, p_)
+            if p_ + 1 >= used:
+                continue
+            se = sb + seg
+            zero = run(sb, se, None)
+            got_loc = np.stack([f32(sloc_off, i, p_, h).reshape(D, D) for h in range(H)])
+            assert tl.rel_l2(got_loc, zero) < 2e-2, (i, p_)
+            X = rng.standard_normal((1, H, D, D)) * 0.3
+            delta = run(sb, se, X) - zero                    # [H, V, K] = X_h M_h^T
+            for h in range(H):
+                M = _decode_m(f32(m_off, i, p_, h), D)
+                assert tl.rel_l2(X[0, h] @ M.T, delta[h]) < 2e-2, (i, p_, h)
+            checked += 1
+    assert checked >= 3

@@ -460,7 +460,7 @@ def test_large_call_form_d32_bf16_gqa():
 @pytest.mark.timeout(600)
 def test_long_l262144_h32_d128_sampled_heads():
     wl = W.long_l262144_h32_d128()
-    heads = [0, 31]
+    heads = [0, 9, 22, 31]
     gpu = tl.run_gpu(wl)
     orc = tl.run_oracle(wl, heads=heads)
     _check(wl, gpu, orc, heads=heads)
