@@ -135,7 +135,10 @@ __global__ void __launch_bounds__(64) state_kernel(Args a) {
 // When the intermediates live in HBM, waves 1 and 4 swap roles (below).
 // Step st (one barrier each): the loaders start chunk st + 2 and wait for
 // chunk st, the compute wave works on chunk st - 1, the output waves on
-// chunk st - 2 and start fetching chunk st.
+// chunk st - 2 and start fetching chunk st.  Larger batches give a
+// workgroup two or four adjacent column tiles (FusedRoles below), which
+// share the W / Ktilde and q / P loads; the context-parallel form runs the
+// same pass over segments of sequences (k5_cp.hip).
 // ===========================================================================
 // L2 warm-up of a chunk ahead of the loaders and output waves: one 4-byte
 // load per 128-byte line of everything the chunk's workgroups will read,
