@@ -66,12 +66,13 @@ def per_token_head_bytes(wl, phase):
     q/k/v/o and intermediates in the compute dtype of width e).
 
     16-bit inputs (the state pass forms the output itself):
-      intra : reads q, k, v, g, beta; writes W, Ktilde, U and the q fragments
-              (64 x D each per chunk-head), the six unmasked 16 x 32 blocks of
-              the masked Q K^T (48 of 64 elements per row) and the 64
-              cumulative log gates
-      state : reads W, Ktilde, U, the q fragments, those Q K^T blocks and the
-              gates; writes o
+      intra : reads q, k, v, g, beta; writes W and U (64 x D each per
+              chunk-head), the normalised k and q fragments (64 x D per chunk
+              and k / q head), the six unmasked 16 x 32 blocks of the masked
+              Q K^T (48 of 64 elements per row) and the 64 cumulative log
+              gates
+      state : reads W, the k fragments, U, the q fragments, those Q K^T
+              blocks and the gates; writes o
     fp32 inputs (separate output pass):
       intra : reads k, v, g, beta; writes W, Ktilde, U and the gates
       state : reads W, Ktilde, U, G_last; writes the chunk-start state
@@ -84,10 +85,11 @@ def per_token_head_bytes(wl, phase):
     hq, hk, hv = wl.q.shape[1], wl.k.shape[1], wl.v.shape[1]
     qf, kf, vf = hq / H, hk / H, hv / H
     if wl.dtype != "f32":
+        inter = (2 + kf + qf) * D * e + 48 * e + 4
         if phase == "intra":
-            return (qf + kf + vf) * D * e + 8 + 4 * D * e + 48 * e + 4
+            return (qf + kf + vf) * D * e + 8 + inter
         if phase == "state":
-            return 4 * D * e + 48 * e + 4 + D * e
+            return inter + D * e
         return 0.0
     st = D * D * e / 64.0          # chunk-start state per token
     if phase == "intra":

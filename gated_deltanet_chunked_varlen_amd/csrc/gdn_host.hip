@@ -106,14 +106,16 @@ Layout plan(const gdn_prefill_params *p) {
   L.cu_chunks = take(sizeof(int32_t) * (size_t)(N + 1));
   L.seq_bos = take(sizeof(int32_t) * (size_t)(N + 1));
   L.n_chunks = take(sizeof(int32_t));
-  L.Wf = take(blocks * 64 * D * es);
-  L.Kf = take(blocks * 64 * D * es);
-  L.Uf = take(blocks * 64 * D * es);
   // 16-bit inputs: the state pass forms the output itself and needs the q and
-  // P fragments instead of chunk-start states and N in memory
+  // P fragments instead of chunk-start states and N in memory; the normalised
+  // k and q fragments are kept once per k / q head (GQA / GVA share them)
   L.fuse = p->qkv_dtype != GDN_F32;
+  const size_t kblocks = L.fuse ? (size_t)cap * p->num_k_heads : blocks;
+  L.Wf = take(blocks * 64 * D * es);
+  L.Kf = take(kblocks * 64 * D * es);
+  L.Uf = take(blocks * 64 * D * es);
   if (L.fuse) {
-    L.Qf = take(blocks * 64 * D * es);
+    L.Qf = take((size_t)cap * p->num_q_heads * 64 * D * es);
     L.Pf = take(blocks * 64 * 64 * es);
   } else {
     L.Nf = take(blocks * 64 * D * es);
@@ -358,9 +360,11 @@ static void fill_args(const gdn_prefill_params *p, const Layout *L, int num_cus,
       a.Qf = ws + L->Qf;
       a.Pf = ws + L->Pf;
       a.fuse = 1;
-      // W, Ktilde, U, q (64 x D each) and P (64 x 64) per chunk-head, 16-bit
-      const int64_t inter = gdn_max_chunks(p->total_tokens, p->num_seqs) * H *
-                            (4 * 64 * D + 64 * 64) * 2;
+      // W, U (64 x D) and P (64 x 64) per chunk-head, K and q (64 x D) per
+      // chunk and k / q head, 16-bit
+      const int64_t inter = gdn_max_chunks(p->total_tokens, p->num_seqs) *
+                            (H * (2 * 64 * D + 64 * 64) +
+                             (int64_t)(p->num_k_heads + p->num_q_heads) * 64 * D) * 2;
       a.warm = inter > kWarmBytes ? 2 : 0;
       a.nt_stores = inter > kWarmBytes ? 1 : 0;
     } else {

@@ -147,6 +147,17 @@ __device__ __forceinline__ void chunk_geometry(const Args &a, int f, int lane, b
   }
 }
 
+// Workspace blocks of the normalised k and q fragments for 16-bit inputs: one
+// per (chunk, k head) and (chunk, q head), shared by every sab head that reads
+// that k or q head (GQA / GVA), at index src_head * cap + f.  ch is the sab
+// head's block index h * cap + f.
+__device__ __forceinline__ int64_t k_block(const Args &a, int64_t ch, int h) {
+  return ch + ((int64_t)(h / (a.H / a.hk)) - h) * a.cap;
+}
+__device__ __forceinline__ int64_t q_block(const Args &a, int64_t ch, int h) {
+  return ch + ((int64_t)(h / (a.H / a.hq)) - h) * a.cap;
+}
+
 // First flat chunk, chunk count, length and first token of sequence seq, for
 // the calling wave.
 __device__ __forceinline__ void seq_geometry(const Args &a, int seq, int lane, int &f0, int &nc,

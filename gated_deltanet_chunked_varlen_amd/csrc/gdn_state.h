@@ -55,6 +55,7 @@ struct ChunkOps {
 template <typename T, int D>
 struct RegOps {
   static constexpr bool kInterleave = false;
+  static constexpr bool kScaleN = false;  // Kf holds Ktilde^T (fp32 inputs)
   const ChunkOps<T, D> &op;
   __device__ __forceinline__ typename Mfma<T>::frag w(int it, int kt) const { return op.w[it][kt]; }
   __device__ __forceinline__ typename Mfma<T>::frag k(int it, int kt) const { return op.k[it][kt]; }
@@ -89,6 +90,17 @@ __device__ __forceinline__ void chunk_step(const Args &a, const Ops &op,
 #pragma unroll
   for (int it = 0; it < 4; ++it) acc[it] = op.uvec(it);
   const float gl = gexp(op.glog());
+  // 16-bit inputs: the gate log-cumsum at this lane's 16 chunk rows (pi
+  // order), read with the W fragments; their decay to the chunk's end is
+  // formed while the first product runs (see below)
+  // (only where K is shared between sab heads; otherwise the workspace holds
+  // Ktilde^T itself)
+  constexpr bool scale_n = Ops::kScaleN;
+  f32x4 grows[4];
+  if constexpr (scale_n) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) grows[j] = op.grow4(16 * j + 4 * (lane >> 4));
+  }
   __builtin_amdgcn_sched_barrier(0);
   // the state as operand fragments (dk in pi order): slot s is S[s / 4][s % 4]
   const float *Sflat = &S[0][0];
@@ -106,7 +118,7 @@ __device__ __forceinline__ void chunk_step(const Args &a, const Ops &op,
       *reinterpret_cast<frag *>(hf + ((int64_t)kt * 64 + lane) * KPL) = sb[kt];
   }
   // N = U + (-W) S      (the workspace holds -W)
-  float accf[16];
+  float accf[16], ndec[16];
   {
 #pragma unroll
     for (int kt = 0; kt < KS_D; ++kt)
@@ -124,6 +136,13 @@ __device__ __forceinline__ void chunk_step(const Args &a, const Ops &op,
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       }
     }
+    if constexpr (scale_n) {
+      const float glast = op.glog();
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ndec[4 * j + r] = gexp(glast - grows[j][r]);
+    }
 #pragma unroll
     for (int it = 0; it < 4; ++it)
 #pragma unroll
@@ -140,62 +159,21 @@ __device__ __forceinline__ void chunk_step(const Args &a, const Ops &op,
       else *reinterpret_cast<frag *>(nfp + ((int64_t)kt * 64 + lane) * KPL) = nf[kt];
     }
   }
+  // Where sab heads share a k head (16-bit inputs), the workspace holds the
+  // normalised K^T once per k head, and the chunk's decay to its end scales
+  // N's rows instead: Ktilde^T N = K^T diag(exp(G_last - G)) N.
+  if constexpr (scale_n) {
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) accf[s2] *= ndec[s2];
+#pragma unroll
+    for (int kt = 0; kt < KS_C; ++kt) nf[kt] = M::pack(accf + kt * KPL);
+  }
   // S' = exp(G_last) S + Ktilde^T N
 #pragma unroll
   for (int it = 0; it < NT; ++it) {
     f32x4 s4 = {S[it][0] * gl, S[it][1] * gl, S[it][2] * gl, S[it][3] * gl};
 #pragma unroll
     for (int kt = 0; kt < KS_C; ++kt) s4 = M::mma(kv[it][kt], nf[kt], s4);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) S[it][r] = s4[r];
-  }
-}
-
-// One chunk of the recurrence with nothing handed off (no chunk-start state,
-// no new values stored): S' = exp(G_last) S + Ktilde^T (U - W S), with U
-// taken as zero when zero_u (a column of a segment's transition matrix
-// evolves like a state column whose U is zero).
-template <typename T, int D>
-__device__ __forceinline__ void chain_step(const ChunkOps<T, D> &op, float (&S)[D / 16][4],
-                                           bool zero_u) {
-  using M = Mfma<T>;
-  using Ge = Geo<T, D>;
-  typedef typename M::frag frag;
-  constexpr int KPL = Ge::KPL, NT = Ge::NT, KS_D = Ge::KS_D, KS_C = Ge::KS_C;
-  const float gl = gexp(op.glog);
-  const float *Sflat = &S[0][0];
-  frag sb[KS_D];
-#pragma unroll
-  for (int kt = 0; kt < KS_D; ++kt) sb[kt] = M::pack(Sflat + kt * KPL);
-  f32x4 acc[4];
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    if (zero_u) {
-      acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-    } else {
-      acc[it] = f32x4{to_f32(op.u[it][0]), to_f32(op.u[it][1]), to_f32(op.u[it][2]),
-                      to_f32(op.u[it][3])};
-    }
-  }
-  // N = U + (-W) S      (the workspace holds -W)
-#pragma unroll
-  for (int kt = 0; kt < KS_D; ++kt)
-#pragma unroll
-    for (int it = 0; it < 4; ++it) acc[it] = M::mma(op.w[it][kt], sb[kt], acc[it]);
-  float accf[16];
-#pragma unroll
-  for (int it = 0; it < 4; ++it)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) accf[4 * it + r] = acc[it][r];
-  frag nf[KS_C];
-#pragma unroll
-  for (int kt = 0; kt < KS_C; ++kt) nf[kt] = M::pack(accf + kt * KPL);
-  // S' = exp(G_last) S + Ktilde^T N
-#pragma unroll
-  for (int it = 0; it < NT; ++it) {
-    f32x4 s4 = {S[it][0] * gl, S[it][1] * gl, S[it][2] * gl, S[it][3] * gl};
-#pragma unroll
-    for (int kt = 0; kt < KS_C; ++kt) s4 = M::mma(op.k[it][kt], nf[kt], s4);
 #pragma unroll
     for (int r = 0; r < 4; ++r) S[it][r] = s4[r];
   }
@@ -312,9 +290,12 @@ struct DmaSlotGeo {
   static constexpr int NP = 2 * NV_W + TW * U_TILE_BYTES / 1024;     // pieces (W, Ktilde, U)
 };
 
-template <typename T, int D, int TW = 1>
+// SCALE: the slot holds the normalised K^T of a k head shared by several sab
+// heads (Ktilde^T otherwise), so the chunk step scales N's rows by the decay.
+template <typename T, int D, int TW = 1, bool SCALE = false>
 struct DmaSlotOps {
   static constexpr bool kInterleave = true;
+  static constexpr bool kScaleN = SCALE;
   typedef typename Mfma<T>::frag frag;
   using SG = DmaSlotGeo<T, D, TW>;
   static constexpr int KPL = Mfma<T>::KPL, KS_D = Geo<T, D>::KS_D, KS_C = Geo<T, D>::KS_C;
@@ -335,6 +316,10 @@ struct DmaSlotOps {
   __device__ __forceinline__ float glog() const {
     return reinterpret_cast<const float *>(slot + SG::G_OFF)[kChunk - 1];
   }
+  // gate log-cumsum at chunk rows p .. p + 3 (p a multiple of 4)
+  __device__ __forceinline__ f32x4 grow4(int p) const {
+    return *reinterpret_cast<const f32x4 *>(slot + SG::G_OFF + 4 * p);
+  }
 };
 
 // Loader wave `part` of NLD: its share of a chunk's pieces (piece i goes to
@@ -351,10 +336,11 @@ struct DmaLoader {
   static constexpr int MIN_PER_PART = NPC / NLD;
   int64_t uoff;
   int lane, part;
+  int64_t kdelta;  // k_block(ch) - ch: the k head's block for this sab head
 
   __device__ __forceinline__ void issue(const Args &a, int64_t ch, unsigned char *slot) const {
     const u32x4 *wf = reinterpret_cast<const u32x4 *>(a.Wf) + ch * BLK + lane;
-    const u32x4 *kf = reinterpret_cast<const u32x4 *>(a.Kf) + ch * BLK + lane;
+    const u32x4 *kf = reinterpret_cast<const u32x4 *>(a.Kf) + (ch + kdelta) * BLK + lane;
     const u32x4 *uf = reinterpret_cast<const u32x4 *>(a.Uf) + ch * BLK + uoff + lane;
 #pragma unroll
     for (int m = 0; m < PPW; ++m) {

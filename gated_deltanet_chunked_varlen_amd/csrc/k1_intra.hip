@@ -310,7 +310,7 @@ struct IntraSmemB {
   float AT[64][68];                   // A, then T; [t][64] = G, [t][65] = beta
 };
 
-template <typename T, int D, bool NTS>
+template <typename T, int D, bool NTS, bool SHK>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) intra_kernel_h(Args a) {
   using M = Mfma<T>;
   typedef typename M::frag frag;
@@ -387,7 +387,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
     const int tt = wave;
     const T(*QR)[136] = reinterpret_cast<const T(*)[136]>(&AT[0][0]);
     T *pf_out = (T *)a.Pf + ch * (int64_t)(64 * 64);
-    T *qf_out = (T *)a.Qf + ch * (int64_t)(64 * D);
+    // q fragments once per q head (the first sab head that reads it writes)
+    T *qf_out = (T *)a.Qf + q_block(a, ch, h) * (int64_t)(64 * D);
+    const bool write_q = h % (H / a.hq) == 0;
     frag pf[KS_C];
     const int t = 16 * tt + c;
     const float gt = AT[t][64];
@@ -416,12 +418,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
     for (int kt = 0; kt < KS_C; ++kt)
       if (2 * kt <= tt)
         st_inter<NTS>(reinterpret_cast<frag *>(pf_out + (((int64_t)tt * KS_C + kt) * 64 + lane) * 8), pf[kt]);
+    if (write_q) {
 #pragma unroll
-    for (int kt = 0; kt < KS_D; ++kt) {
-      frag qf;
+      for (int kt = 0; kt < KS_D; ++kt) {
+        frag qf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qf[e] = QR[t][pi_idx(g, kt * 8 + e)];
-      st_inter<NTS>(reinterpret_cast<frag *>(qf_out + (((int64_t)tt * KS_D + kt) * 64 + lane) * 8), qf);
+        for (int e = 0; e < 8; ++e) qf[e] = QR[t][pi_idx(g, kt * 8 + e)];
+        st_inter<NTS>(reinterpret_cast<frag *>(qf_out + (((int64_t)tt * KS_D + kt) * 64 + lane) * 8), qf);
+      }
     }
     lds_sync();  // q is consumed: A may overwrite the buffer
   }
@@ -540,23 +544,31 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
     for (int kt = 0; kt < KS_D; ++kt)
       st_inter<NTS>(reinterpret_cast<frag *>(wf + ((int64_t)kt * 64 + lane) * 8), out[kt]);
   }
-  // ---- Ktilde^T fragments: rows pi(g, 8kt + e) of k column 16 it2 + c ------
-  {
+  // ---- K^T fragments: rows pi(g, 8kt + e) of k column 16 it2 + c ----------
+  // Where sab heads share a k head, the normalised k once per k head (the
+  // first sab head that reads it writes), and the state pass applies each sab
+  // head's decay to the chunk end, exp(G_last - G_t), to N's rows instead
+  // (Ktilde^T N = K^T diag(.) N); otherwise Ktilde^T itself.
+  if (h % (H / a.hk) == 0) {
+    constexpr bool shared = SHK;  // sab heads share k heads
     const float glast = AT[63][64];
-    T *kf = (T *)a.Kf + ch * (int64_t)(64 * D);
+    T *kf = (T *)a.Kf + k_block(a, ch, h) * (int64_t)(64 * D);
 #pragma unroll
     for (int q = 0; q < NT * KS_C / 4; ++q) {
       const int fidx = wave + 4 * q;  // fragment block (row tile it2, k-step kt)
       const int kt = fidx % KS_C, it2 = fidx / KS_C;
       const int r0 = 32 * kt + 4 * g, r1 = r0 + 16;
-      const frag kv = lds_col_frag(&KV[0][0], LDK, r0, r1, 16 * it2, c);
-      float y[8];
+      frag kv = lds_col_frag(&KV[0][0], LDK, r0, r1, 16 * it2, c);
+      if (!shared) {
+        float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = (e < 4 ? r0 : r1) + (e & 3);
-        y[e] = (float)kv[e] * gexp(glast - AT[j][64]);
+        for (int e = 0; e < 8; ++e) {
+          const int j = (e < 4 ? r0 : r1) + (e & 3);
+          y[e] = (float)kv[e] * gexp(glast - AT[j][64]);
+        }
+        kv = M::pack(y);
       }
-      st_inter<NTS>(reinterpret_cast<frag *>(kf + ((int64_t)fidx * 64 + lane) * 8), M::pack(y));
+      st_inter<NTS>(reinterpret_cast<frag *>(kf + ((int64_t)fidx * 64 + lane) * 8), kv);
     }
   }
   lds_sync();  // k rows consumed
@@ -594,23 +606,28 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
   }
 }
 
-template <typename T, int D, bool NTS>
+template <typename T, int D, bool NTS, bool SHK>
 static hipError_t launch_intra_h_nt(const Args &a, hipStream_t s) {
   const size_t smem = sizeof(IntraSmemB<T, D>);
   static std::atomic<uint64_t> lds_set{0};
   {
-    const hipError_t e = set_dynamic_lds((const void *)intra_kernel_h<T, D, NTS>, (int)smem, lds_set);
+    const hipError_t e = set_dynamic_lds((const void *)intra_kernel_h<T, D, NTS, SHK>, (int)smem, lds_set);
     if (e != hipSuccess) return e;
   }
   const int64_t blocks = a.cap * a.H;
   if (blocks == 0) return hipSuccess;
-  intra_kernel_h<T, D, NTS><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
+  intra_kernel_h<T, D, NTS, SHK><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_intra_h(const Args &a, hipStream_t s) {
-  return a.nt_stores ? launch_intra_h_nt<T, D, true>(a, s) : launch_intra_h_nt<T, D, false>(a, s);
+  // SHK: the sab heads share k heads, whose normalised K^T is stored once
+  if (a.H != a.hk)
+    return a.nt_stores ? launch_intra_h_nt<T, D, true, true>(a, s)
+                       : launch_intra_h_nt<T, D, false, true>(a, s);
+  return a.nt_stores ? launch_intra_h_nt<T, D, true, false>(a, s)
+                     : launch_intra_h_nt<T, D, false, false>(a, s);
 }
 
 hipError_t launch_intra(const Args &a, hipStream_t s) {

@@ -160,11 +160,11 @@ struct L2Warm {
   // tiles are TW jw .. TW jw + TW - 1.  touch_shared: the workgroup's share
   // of the lines all NWG workgroups read; touch_own: its U tiles and the
   // gate row.
-  __device__ __forceinline__ static void touch_shared(const Args &a, int64_t ch, int jw, int lane,
-                                                      unsigned char *junk) {
+  __device__ __forceinline__ static void touch_shared(const Args &a, int64_t ch, int h, int jw,
+                                                      int lane, unsigned char *junk) {
     const unsigned char *wf = (const unsigned char *)a.Wf + ch * (WL * LINE);
-    const unsigned char *kf = (const unsigned char *)a.Kf + ch * (WL * LINE);
-    const unsigned char *qf = (const unsigned char *)a.Qf + ch * (WL * LINE);
+    const unsigned char *kf = (const unsigned char *)a.Kf + k_block(a, ch, h) * (WL * LINE);
+    const unsigned char *qf = (const unsigned char *)a.Qf + q_block(a, ch, h) * (WL * LINE);
     const unsigned char *pf = (const unsigned char *)a.Pf + ch * (PL * LINE);
 #pragma unroll
     for (int l0 = 0; l0 < SHARED; l0 += NWG * 64) {
@@ -188,17 +188,17 @@ struct L2Warm {
       dma4(l < UL ? uf + l * LINE : gw + (l - UL) * LINE, junk);
     }
   }
-  __device__ __forceinline__ static void touch(const Args &a, int64_t ch, int jw, int lane,
+  __device__ __forceinline__ static void touch(const Args &a, int64_t ch, int h, int jw, int lane,
                                                unsigned char *junk) {
-    touch_shared(a, ch, jw, lane, junk);
+    touch_shared(a, ch, h, jw, lane, junk);
     touch_own(a, ch, jw, lane, junk);
   }
 };
 
 // The compute wave's operands when its U tile comes through its own
 // registers (four-tile workgroups, whose LDS slots hold W and Ktilde only).
-template <typename T, int D>
-struct SlotRegUOps : DmaSlotOps<T, D, 0> {
+template <typename T, int D, bool SCALE>
+struct SlotRegUOps : DmaSlotOps<T, D, 0, SCALE> {
   const T (*u)[4];
   __device__ __forceinline__ f32x4 uvec(int it) const {
     return f32x4{to_f32(u[it][0]), to_f32(u[it][1]), to_f32(u[it][2]), to_f32(u[it][3])};
@@ -232,10 +232,11 @@ struct OutRegs {
   frag p0, p1[KS_C];
   float g[2];
 
-  __device__ __forceinline__ void issue(const Args &a, int64_t ch, int lane, int ow) {
+  __device__ __forceinline__ void issue(const Args &a, int64_t ch, int h, int lane, int ow) {
     static_assert(KS_C == 2, "64-token chunks: two k-steps over a chunk");
     const int tt0 = ow, tt1 = 3 - ow;
-    const frag *qf = reinterpret_cast<const frag *>(reinterpret_cast<const u32x4 *>(a.Qf) + ch * QBLK) + lane;
+    const frag *qf = reinterpret_cast<const frag *>(reinterpret_cast<const u32x4 *>(a.Qf) +
+                                                    q_block(a, ch, h) * QBLK) + lane;
     const frag *pf = reinterpret_cast<const frag *>(reinterpret_cast<const u32x4 *>(a.Pf) + ch * PBLK) + lane;
 #pragma unroll
     for (int kt = 0; kt < KS_D; ++kt) {
@@ -306,7 +307,7 @@ __device__ __forceinline__ void output_wave_step(const Args &a, int st, int nc, 
                                                  OutRegs<T, D> &into, const OutRegs<T, D> &proc,
                                                  const typename Mfma<T>::frag (*xbuf)[2][(Geo<T, D>::KS_D + Geo<T, D>::KS_C) * 64]) {
   lds_sync();
-  into.issue(a, ch0 + (int64_t)min(st, nc - 1), lane, ow);
+  into.issue(a, ch0 + (int64_t)min(st, nc - 1), h, lane, ow);
   const int oc = st - 2;
   const int64_t tok0 = (int64_t)sbos + (int64_t)kChunk * oc;
   const int rows = min(kChunk, len - kChunk * oc);
@@ -377,7 +378,7 @@ template <> struct FusedRoles<4> {
 // segment that holds the sequence's last chunk.  Segments past a sequence's
 // end exit at once (segment 0 still runs for an empty sequence, whose final
 // state is its initial state).
-template <typename T, int D, int TW, bool CP = false>
+template <typename T, int D, int TW, bool CP = false, bool SHK = false>
 __global__ void __launch_bounds__(64 * FusedRoles<TW>::kWaves)
 state_output_kernel(Args a) {
   using R = FusedRoles<TW>;
@@ -467,7 +468,7 @@ state_output_kernel(Args a) {
         fill.load(a, ch0 + (int64_t)min(st, nc - 1), jg, lane);
         lds_sync();
         const int cc = st - 1;
-        SlotRegUOps<T, D> op;
+        SlotRegUOps<T, D, SHK> op;
         op.slot = cslots[cc % NSLOT];
         op.lane = lane;
         op.utile = 0;
@@ -491,7 +492,7 @@ state_output_kernel(Args a) {
         lds_sync();
         if (st == 0 || st > nc) continue;
         const int cc = st - 1;
-        const DmaSlotOps<T, D, TW> op{cslots[cc % NSLOT], lane, ct};
+        const DmaSlotOps<T, D, TW, SHK> op{cslots[cc % NSLOT], lane, ct};
         chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[ct][cc & 1]);
         checkpoint(cc);
       }
@@ -509,9 +510,9 @@ state_output_kernel(Args a) {
     // steps 0 and 1 only fetch; step st >= 2 fetches chunk st and outputs
     // chunk st - 2 (ring slot st % 3 either way)
     lds_sync();
-    r0.issue(a, ch0, lane, ow);
+    r0.issue(a, ch0, h, lane, ow);
     lds_sync();
-    r1.issue(a, ch0 + (int64_t)min(1, nc - 1), lane, ow);
+    r1.issue(a, ch0 + (int64_t)min(1, nc - 1), h, lane, ow);
     int st = 2;
     for (; st + 3 <= nc + 2; st += 3) {
       output_wave_step<T, D, TW>(a, st, nc, len, sbos, ch0, jg0, h, lane, ow, r2, r0, xbuf);
@@ -526,15 +527,15 @@ state_output_kernel(Args a) {
   } else if (wave == R::warm_wave(hbm)) {
     // ---------------- L2 warm-up wave ---------------------------------------
     const int ahead = a.warm;
-    for (int cc = 0; cc < ahead && cc < nc; ++cc) L2Warm<T, D, TW>::touch(a, ch0 + cc, jw, lane, junk);
+    for (int cc = 0; cc < ahead && cc < nc; ++cc) L2Warm<T, D, TW>::touch(a, ch0 + cc, h, jw, lane, junk);
     for (int st = 0; st <= nc + 1; ++st) {
       __builtin_amdgcn_s_barrier();
-      if (ahead > 0 && st + ahead < nc) L2Warm<T, D, TW>::touch(a, ch0 + (int64_t)(st + ahead), jw, lane, junk);
+      if (ahead > 0 && st + ahead < nc) L2Warm<T, D, TW>::touch(a, ch0 + (int64_t)(st + ahead), h, jw, lane, junk);
     }
     wait_vm<0>();
   } else if (part >= 0) {
     // ---------------- loader waves ------------------------------------------
-    const LD ld{(int64_t)jg0 * (SG::U_TILE_BYTES / 16), lane, part};
+    const LD ld{(int64_t)jg0 * (SG::U_TILE_BYTES / 16), lane, part, k_block(a, ch0, h) - ch0};
     for (int cc = 0; cc < AHEAD && cc < nc; ++cc) ld.issue(a, ch0 + (int64_t)cc, cslots[cc]);
     for (int st = 0; st <= nc + 1; ++st) {
       __builtin_amdgcn_s_barrier();
@@ -562,15 +563,18 @@ static hipError_t launch_state_output_tw(const Args &a, hipStream_t s) {
   const int64_t units = (int64_t)a.N * a.H * (cp ? a.cp_nseg : 1);
   const int64_t blocks = ((units + 7) / 8) * 8 * NWG;
   const dim3 grid((unsigned)blocks), block(64 * FusedRoles<TW>::kWaves);
+  const bool shk = a.H != a.hk;   // sab heads share k heads (GQA / GVA)
   if constexpr (D == 128) {
     if (cp) {
-      state_output_kernel<T, D, TW, true><<<grid, block, 0, s>>>(a);
+      if (shk) state_output_kernel<T, D, TW, true, true><<<grid, block, 0, s>>>(a);
+      else state_output_kernel<T, D, TW, true, false><<<grid, block, 0, s>>>(a);
       return hipGetLastError();
     }
   } else {
     if (cp) return hipErrorInvalidValue;
   }
-  state_output_kernel<T, D, TW><<<grid, block, 0, s>>>(a);
+  if (shk) state_output_kernel<T, D, TW, false, true><<<grid, block, 0, s>>>(a);
+  else state_output_kernel<T, D, TW, false, false><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -92,6 +92,22 @@ __device__ __forceinline__ void pair_step(const Ops &op, float (&S0)[D / 16][4],
       n0[4 * it + r] = acc0[it][r];
       n1[4 * it + r] = acc1[it][r];
     }
+  // where sab heads share a k head the slot holds the normalised K^T, and
+  // the decay to the chunk's end scales N's rows (Ktilde^T N = K^T diag(.) N)
+  if constexpr (Ops::kScaleN) {
+    const int g = (op.lane >> 4);
+    const float glast = op.glog();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 gv = op.grow4(16 * j + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = gexp(glast - gv[r]);
+        n0[4 * j + r] *= f;
+        n1[4 * j + r] *= f;
+      }
+    }
+  }
   frag nf0[KS_C], nf1[KS_C];
 #pragma unroll
   for (int kt = 0; kt < KS_C; ++kt) {
@@ -140,10 +156,10 @@ struct TransWarm {
   static constexpr int UL = kCpTW * DmaSlotGeo<T, D>::U_TILE_BYTES / LINE;
   static constexpr int GL = 64 * 4 / LINE;
   static_assert(UL + GL <= 64, "one line per lane");
-  __device__ __forceinline__ static void touch(const Args &a, int64_t ch, int jw, int lane,
+  __device__ __forceinline__ static void touch(const Args &a, int64_t ch, int h, int jw, int lane,
                                                unsigned char *junk) {
     const unsigned char *wf = (const unsigned char *)a.Wf + ch * (WL * LINE);
-    const unsigned char *kf = (const unsigned char *)a.Kf + ch * (WL * LINE);
+    const unsigned char *kf = (const unsigned char *)a.Kf + k_block(a, ch, h) * (WL * LINE);
 #pragma unroll
     for (int l0 = 0; l0 < SHARED; l0 += NWG * 64) {
       const int l = min(l0 + jw + NWG * lane, SHARED - 1);
@@ -157,7 +173,7 @@ struct TransWarm {
   }
 };
 
-template <typename T, int D>
+template <typename T, int D, bool SHK>
 __global__ void __launch_bounds__(320) cp_transition_kernel(Args a) {
   constexpr int NT = D / 16, NWG = NT / kCpTW, NLD = 2, NSLOT = kCpSlots, AHEAD = NSLOT - 2;
   using SG = DmaSlotGeo<T, D, kCpTW>;
@@ -199,7 +215,7 @@ __global__ void __launch_bounds__(320) cp_transition_kernel(Args a) {
       lds_sync();
       if (st == 0) continue;
       const int cc = st - 1;
-      const DmaSlotOps<T, D, kCpTW> op{cslots[cc % NSLOT], lane, wave};
+      const DmaSlotOps<T, D, kCpTW, SHK> op{cslots[cc % NSLOT], lane, wave};
       pair_step<T, D>(op, S0, S1);
     }
     const int64_t str[4] = {0, 0, (int64_t)D, 1};
@@ -218,15 +234,16 @@ __global__ void __launch_bounds__(320) cp_transition_kernel(Args a) {
   } else if (wave == kCpTW + NLD) {
     const int ahead = a.warm;
     for (int cc = AHEAD; cc < AHEAD + ahead && cc < n; ++cc)
-      TransWarm<T, D>::touch(a, ch0 + cc, jw, lane, junk);
+      TransWarm<T, D>::touch(a, ch0 + cc, h, jw, lane, junk);
     for (int st = 0; st <= n; ++st) {
       __builtin_amdgcn_s_barrier();
       if (ahead > 0 && st + AHEAD + ahead < n)
-        TransWarm<T, D>::touch(a, ch0 + (int64_t)(st + AHEAD + ahead), jw, lane, junk);
+        TransWarm<T, D>::touch(a, ch0 + (int64_t)(st + AHEAD + ahead), h, jw, lane, junk);
     }
     wait_vm<0>();
   } else {
-    const LD ld{(int64_t)kCpTW * jw * (SG::U_TILE_BYTES / 16), lane, wave - kCpTW};
+    const LD ld{(int64_t)kCpTW * jw * (SG::U_TILE_BYTES / 16), lane, wave - kCpTW,
+                k_block(a, ch0, h) - ch0};
     for (int cc = 0; cc < AHEAD && cc < n; ++cc) ld.issue(a, ch0 + (int64_t)cc, cslots[cc]);
     for (int st = 0; st <= n; ++st) {
       __builtin_amdgcn_s_barrier();
@@ -355,10 +372,15 @@ hipError_t launch_cp_transition(const Args &a, hipStream_t s) {
   const int64_t units = (int64_t)a.N * a.cp_nseg * a.H;
   if (units == 0 || a.D != D) return units == 0 ? hipSuccess : hipErrorInvalidValue;
   const int64_t blocks = ((units + 7) / 8) * 8 * NWG;
-  if (a.dtype == GDN_F16)
-    cp_transition_kernel<f16, D><<<dim3((unsigned)blocks), dim3(320), 0, s>>>(a);
-  else
-    cp_transition_kernel<bf16, D><<<dim3((unsigned)blocks), dim3(320), 0, s>>>(a);
+  const dim3 grid((unsigned)blocks), block(320);
+  const bool shk = a.H != a.hk;   // sab heads share k heads (GQA / GVA)
+  if (a.dtype == GDN_F16) {
+    if (shk) cp_transition_kernel<f16, D, true><<<grid, block, 0, s>>>(a);
+    else cp_transition_kernel<f16, D, false><<<grid, block, 0, s>>>(a);
+  } else {
+    if (shk) cp_transition_kernel<bf16, D, true><<<grid, block, 0, s>>>(a);
+    else cp_transition_kernel<bf16, D, false><<<grid, block, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -328,3 +328,19 @@ def test_context_parallel_arguments_checked():
     big = lambda **e: L.gdn_prefill_workspace_size(ctypes.byref(
         _params(T=4096, N=2, hq=16, hk=16, hv=16, extra=e)))
     assert big(use_cp=nat.CP_AUTO) == big(use_cp=nat.CP_OFF)
+
+
+def test_shared_k_and_q_fragments_sized_per_source_head():
+    # 16-bit inputs keep the normalised k and q fragments once per (chunk, k
+    # head) and (chunk, q head): a GVA call with 16 q/k heads and 32 v heads
+    # needs 2 x 16 fewer 64 x D blocks per chunk than one with 32 of each
+    nat = _lib()
+    L = nat.lib()
+    ws = lambda hq, hk, hv: L.gdn_prefill_workspace_size(ctypes.byref(
+        _params(T=4096, N=2, hq=hq, hk=hk, hv=hv, extra=dict(use_cp=nat.CP_OFF))))
+    cap = L.gdn_max_chunks(4096, 2)
+    assert ws(32, 32, 32) - ws(16, 16, 32) == 2 * 16 * cap * 64 * 128 * 2
+    # fp32 inputs keep Ktilde per sab head (no q fragments)
+    ws32 = lambda hq, hk, hv: L.gdn_prefill_workspace_size(ctypes.byref(
+        _params(T=4096, N=2, hq=hq, hk=hk, hv=hv, dtype=nat.GDN_F32)))
+    assert ws32(32, 32, 32) == ws32(16, 16, 32)
