@@ -402,9 +402,20 @@ state_output_kernel(Args a) {
   const int b = blockIdx.x;
   const int jw = (b >> 3) % NWG;       // workgroup within its (sequence, head)
   const int jg0 = jw * TW;             // first column tile
-  const int u = (b / (8 * NWG)) * 8 + (b & 7);
   const int H = a.H;
   const int NS = CP ? a.cp_nseg : 1;
+  // units in XCD round-robin order (consecutive ids go to the 8 XCDs in turn)
+  const int ub = (b / (8 * NWG)) * 8 + (b & 7);
+  int u = ub;
+  if constexpr (SHK) {
+    // the R sab heads of one k head on one XCD, so that the K^T (and q)
+    // blocks they share meet in its L2: unit ub = 8 R m + 8 j + x is sab
+    // head j of k-head unit 8 m + x (the grid is padded to whole groups)
+    const int R = H / a.hk;
+    const int ku = (ub / (8 * R)) * 8 + (ub & 7), j = (ub / 8) % R;
+    u = (ku / a.hk) * H + (ku % a.hk) * R + j;
+    if (ku >= a.N * NS * a.hk) return;
+  }
   if (u >= a.N * NS * H) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = u % H;
@@ -560,8 +571,14 @@ template <typename T, int D, int TW>
 static hipError_t launch_state_output_tw(const Args &a, hipStream_t s) {
   constexpr int NWG = D / 16 / TW;
   const bool cp = a.cp_nseg > 0;
-  const int64_t units = (int64_t)a.N * a.H * (cp ? a.cp_nseg : 1);
-  const int64_t blocks = ((units + 7) / 8) * 8 * NWG;
+  const int64_t ns = cp ? a.cp_nseg : 1;
+  const int64_t units = (int64_t)a.N * a.H * ns;
+  int64_t blocks = ((units + 7) / 8) * 8 * NWG;
+  if (a.H != a.hk) {
+    // k-head groups of H / hk units, whole groups of 8 (see the kernel)
+    const int64_t kunits = (int64_t)a.N * a.hk * ns;
+    blocks = ((kunits + 7) / 8) * 8 * (a.H / a.hk) * NWG;
+  }
   const dim3 grid((unsigned)blocks), block(64 * FusedRoles<TW>::kWaves);
   const bool shk = a.H != a.hk;   // sab heads share k heads (GQA / GVA)
   if constexpr (D == 128) {
