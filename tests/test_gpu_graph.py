@@ -202,3 +202,30 @@ def test_workspace_cache_reused_across_rotating_buffers():
     torch.cuda.synchronize()
     assert len(api._ws_cache) == 2
     api.clear_workspace_cache()
+
+
+def test_context_parallel_call_replays_bit_equal_to_eager():
+    # the context-parallel form (four kernels, no memset) under capture, with
+    # rotated buffer sets: each replay equals an eager call bit for bit
+    lengths, H, D = [1000, 333], 2, 128
+    mk = lambda seed: W.make(seed, lengths, H, H, H, D, "bf16", l2norm_in_kernel=True,
+                             init="seq", init_std=0.3)
+    sets = [_buffer_set(130 + i, lengths, H, D, mk) for i in range(2)]
+    graphs = api.PrefillGraphs()
+    seed = 140
+    for rnd in range(2):
+        for s in sets:
+            _refill(s, mk(seed))
+            seed += 1
+            got_out, got_fin = graphs(s["q"], s["k"], s["v"], s["g"], s["beta"],
+                                      use_cp=True, _cp_chunk_len=256, **_args(s))
+            torch.cuda.synchronize()
+            got_out, got_fin = got_out.clone(), got_fin.clone()
+            e_out, e_fin = chunk_gated_delta_rule(
+                s["q"], s["k"], s["v"], s["g"], s["beta"], initial_state=s["initial_state"],
+                output_final_state=True, cu_seqlens=s["cu_seqlens"],
+                use_qk_l2norm_in_kernel=True, use_cp=True, _cp_chunk_len=256)
+            torch.cuda.synchronize()
+            assert int(s["st"].item()) == 0
+            assert torch.equal(got_out, e_out) and torch.equal(got_fin, e_fin), (rnd, seed)
+    assert graphs.graphs_captured == 2

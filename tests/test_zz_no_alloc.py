@@ -32,7 +32,7 @@ def _gpu():
     yield
 
 
-def _both(wl):
+def _both(wl, **extra):
     """Run ``wl`` through gdn_prefill (fresh workspace) and through
     gdn_prefill_noalloc into separate output buffers; returns both results as
     tensors."""
@@ -55,6 +55,7 @@ def _both(wl):
                       checkpoint_every_n_tokens=wl.checkpoint_every)
         st = torch.full((1,), -1, dtype=torch.int32, device="cuda")
         kw["status"] = st
+        kw.update(extra)
         torch.cuda.synchronize()
         if noalloc:
             before = torch.cuda.memory_allocated()
@@ -111,3 +112,11 @@ def test_noalloc_rejects_a_call_larger_than_the_scratch():
     assert rc == nat.ERR_CODE["GDN_ERR_SCRATCH"]
     with pytest.raises(ValueError):
         api.chunk_gated_delta_rule_noalloc(d["q"], d["k"], d["v"])      # no output buffer
+
+
+def test_noalloc_context_parallel_matches_prefill():
+    # the context-parallel form takes its segment buffers from the scratch too
+    wl = W.make(104, [1500, 700], 2, 2, 2, 128, "bf16", l2norm_in_kernel=True, init="seq",
+                init_std=0.3)
+    (o1, f1, _), (o2, f2, _) = _both(wl, use_cp=True, _cp_chunk_len=256)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
