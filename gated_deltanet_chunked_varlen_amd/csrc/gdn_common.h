@@ -271,10 +271,12 @@ __device__ __forceinline__ void load_row_part(const Tin *row, int p, float (&x)[
 // optionally normalised with row_inv_norm, rounded back to the input type:
 // NV = D / 32 fragments of 8 elements, fragment i holding row elements
 // 32 i + 8 p .. + 7.  The intra-chunk and output passes both use this, so they
-// see the same k rows.
+// see the same k rows.  inv (optional) receives the factor applied: the
+// row's inverse norm, or 1 without normalisation.
 template <typename T, int D>
 __device__ __forceinline__ void load_norm_row16(const T *row, int p, bool valid, bool l2norm,
-                                                typename Mfma<T>::frag (&out)[D / 32]) {
+                                                typename Mfma<T>::frag (&out)[D / 32],
+                                                float *inv_out = nullptr) {
   typedef typename Mfma<T>::frag frag;
   constexpr int NV = D / 32;
   u32x4 raw[NV];
@@ -284,6 +286,7 @@ __device__ __forceinline__ void load_norm_row16(const T *row, int p, bool valid,
   if (!l2norm) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) out[i] = __builtin_bit_cast(frag, raw[i]);
+    if (inv_out) *inv_out = 1.f;
     return;
   }
   float x[D / 4];
@@ -294,6 +297,7 @@ __device__ __forceinline__ void load_norm_row16(const T *row, int p, bool valid,
     for (int e = 0; e < 8; ++e) x[8 * i + e] = (float)r8[e];
   }
   const float inv = row_inv_norm<D>(x);
+  if (inv_out) *inv_out = inv;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const f32x8 y = {x[8 * i] * inv,     x[8 * i + 1] * inv, x[8 * i + 2] * inv,

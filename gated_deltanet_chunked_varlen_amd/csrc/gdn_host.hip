@@ -87,7 +87,7 @@ CpConfig cp_config(const gdn_prefill_params *p) {
 }
 
 struct Layout {
-  size_t chunk_idx, chunk_tok, cu_chunks, seq_bos, n_chunks, Wf, Kf, Uf, Hf, Nf, Qf, Pf, Gw;
+  size_t chunk_idx, chunk_tok, cu_chunks, seq_bos, n_chunks, Wf, Kf, Uf, Hf, Nf, Qf, Pf, Gw, Bw;
   size_t cp_start, cp_sloc, cp_m, total;
   bool fuse;
   CpConfig cp;
@@ -122,6 +122,8 @@ Layout plan(const gdn_prefill_params *p) {
     L.Hf = take(blocks * D * D * es);
   }
   L.Gw = take(blocks * 64 * sizeof(float));
+  // the T form's row scales (two rows of 64 floats per chunk-head)
+  if (L.fuse) L.Bw = take(blocks * 128 * sizeof(float));
   L.cp = cp_config(p);
   if (L.cp.nseg > 0) {
     // fp32 [N][nseg][H][D][D] each: segment start states, and each segment's
@@ -372,6 +374,13 @@ static void fill_args(const gdn_prefill_params *p, const Layout *L, int num_cus,
       a.Nf = ws + L->Nf;
     }
     a.Gw = (float *)(ws + L->Gw);
+    if (L->fuse) {
+      a.Bw = (float *)(ws + L->Bw);
+      // the four-tile state pass (at least four column tiles per CU) in its
+      // T form: 16-bit D = 128 without context parallelism
+      const int64_t tiles = (int64_t)p->num_seqs * H * (D / 16);
+      a.tform = (D == 128 && L->cp.nseg == 0 && num_cus > 0 && tiles >= 4ll * num_cus) ? 1 : 0;
+    }
     if (L->cp.nseg > 0) {
       a.cp_seg = L->cp.seg;
       a.cp_nseg = L->cp.nseg;

@@ -61,6 +61,14 @@ struct Args {
   void *Qf, *Pf;
   int32_t fuse;
   float *Gw;
+  // T form of the four-tile fused pass (tform != 0, set by the host when the
+  // state pass takes that form): Wf holds -T diag(beta exp(G)) per chunk-head
+  // as 64 x 64 operand fragments instead of -W, Kf is not written, and Bw
+  // holds per chunk-head two rows of 64 floats: 1 / |k_t| and
+  // exp(G_last - G_t) / |k_t| (0 past the chunk's end); the state pass reads
+  // the raw k rows from the input
+  float *Bw;
+  int32_t tform;
   // states
   const void *init;
   int32_t init_dtype;

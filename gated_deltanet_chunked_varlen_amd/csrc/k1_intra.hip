@@ -310,7 +310,7 @@ struct IntraSmemB {
   float AT[64][68];                   // A, then T; [t][64] = G, [t][65] = beta
 };
 
-template <typename T, int D, bool NTS, bool SHK>
+template <typename T, int D, bool NTS, bool SHK, bool TF>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) intra_kernel_h(Args a) {
   using M = Mfma<T>;
   typedef typename M::frag frag;
@@ -343,10 +343,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
     for (int i = 0; i < NV; ++i)
       vraw[i] = valid ? *reinterpret_cast<const u32x4 *>(vrow + 32 * i + 8 * lp) : u32x4{0, 0, 0, 0};
     frag kn[NV];
+    float kinv;
     load_norm_row16<T, D>((const T *)a.k + ((bos + lt) * a.hk + kh) * D, lp, valid,
-                          a.l2norm != 0, kn);
+                          a.l2norm != 0, kn, &kinv);
 #pragma unroll
     for (int i = 0; i < NV; ++i) *reinterpret_cast<frag *>(&KV[lt][32 * i + 8 * lp]) = kn[i];
+    // T form: the k row's normalisation factor (0 past the chunk's end) in
+    // column 66 of the A/T buffer, beside the gate and beta columns
+    if (TF && lp == 0) AT[lt][66] = valid ? kinv : 0.f;
     if (a.fuse) {
       // q rows (normalised) go to the A/T buffer until A is formed: row t at
       // byte 272 t, below the G / beta columns (bytes 256 .. 263 of the row)
@@ -509,6 +513,31 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
   }
 
   const int w = wave;  // token tile of this wave
+  if constexpr (TF) {
+    // ---- T form: -T diag(beta exp(G)) and the row scales ---------------------
+    // The state pass forms W S = T diag(beta exp(G)) diag(1/|k|) (K S) from
+    // the raw k rows, so instead of -W this stores the 64 x 64 factor as
+    // operand fragments: [w][kt][lane] = rows 16 w + c, columns (tokens) in
+    // pi order, matching the pi order of K S's result rows; and per token
+    // 1/|k_t| and exp(G_last - G_t) / |k_t| (Ktilde^T N = K^T diag(that) N).
+    T *tf = (T *)a.Wf + ch * (int64_t)(64 * 64) + (int64_t)w * KS_C * 64 * 8;
+#pragma unroll
+    for (int kt = 0; kt < KS_C; ++kt) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 32 * kt + 16 * (e >> 2) + 4 * g + (e & 3);
+        y[e] = -AT[16 * w + c][j] * AT[j][65] * gexp(AT[j][64]);
+      }
+      st_inter<NTS>(reinterpret_cast<frag *>(tf + ((int64_t)kt * 64 + lane) * 8), M::pack(y));
+    }
+    if (wave == 0) {
+      const float inv = AT[lane][66];
+      float *bw = a.Bw + ch * 128;
+      bw[lane] = inv;
+      bw[64 + lane] = gexp(AT[63][64] - AT[lane][64]) * inv;
+    }
+  } else {
   // ---- W (as W^T tiles): A operand = k columns via transposed reads --------
   {
     frag bw[KS_C];
@@ -571,6 +600,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
       st_inter<NTS>(reinterpret_cast<frag *>(kf + ((int64_t)fidx * 64 + lane) * 8), kv);
     }
   }
+  }  // W form
   lds_sync();  // k rows consumed
 #pragma unroll
   for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4 *>(&KV[lt][32 * i + 8 * lp]) = vraw[i];
@@ -606,22 +636,31 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
   }
 }
 
-template <typename T, int D, bool NTS, bool SHK>
+template <typename T, int D, bool NTS, bool SHK, bool TF = false>
 static hipError_t launch_intra_h_nt(const Args &a, hipStream_t s) {
   const size_t smem = sizeof(IntraSmemB<T, D>);
   static std::atomic<uint64_t> lds_set{0};
   {
-    const hipError_t e = set_dynamic_lds((const void *)intra_kernel_h<T, D, NTS, SHK>, (int)smem, lds_set);
+    const hipError_t e = set_dynamic_lds((const void *)intra_kernel_h<T, D, NTS, SHK, TF>, (int)smem, lds_set);
     if (e != hipSuccess) return e;
   }
   const int64_t blocks = a.cap * a.H;
   if (blocks == 0) return hipSuccess;
-  intra_kernel_h<T, D, NTS, SHK><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
+  intra_kernel_h<T, D, NTS, SHK, TF><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_intra_h(const Args &a, hipStream_t s) {
+  // T form (four-tile state pass, D = 128): K^T is not stored, so sab heads
+  // sharing k heads need no variant of their own
+  if constexpr (D == 128) {
+    if (a.tform)
+      return a.nt_stores ? launch_intra_h_nt<T, D, true, false, true>(a, s)
+                         : launch_intra_h_nt<T, D, false, false, true>(a, s);
+  } else {
+    if (a.tform) return hipErrorInvalidValue;
+  }
   // SHK: the sab heads share k heads, whose normalised K^T is stored once
   if (a.H != a.hk)
     return a.nt_stores ? launch_intra_h_nt<T, D, true, true>(a, s)

@@ -219,6 +219,179 @@ struct UTile {
 };
 
 
+// ---------------------------------------------------------------------------
+// T form of the four-tile pass (16-bit, D = 128).  With S the chunk-start
+// state, K the chunk's raw k rows, n_t = |k_t| (1 without normalisation) and
+// T = (I + A)^-1 from the intra-chunk pass:
+//
+//   W S          = T diag(beta exp(G)) diag(1/n) (K S)
+//   Ktilde^T N   = K^T diag(exp(G_last - G) / n) N
+//
+// so the slot holds the raw k rows (read twice: as rows for K S, and through
+// transposed reads for K^T) and the 64 x 64 factor -T diag(beta exp(G))
+// instead of -W and Ktilde^T: 24 KB of operands per chunk instead of 32, and
+// the intra-chunk pass writes 8 KB per chunk-head instead of -W and Ktilde^T
+// (16 KB each).  The k rows come straight from the input (shared by the sab
+// heads of a k head).  A slot: [k rows, 16-byte units of row r permuted by
+// XOR with r mod 16][-T diag(beta exp G) fragments][gate row][1/n row]
+// [exp(G_last - G)/n row].  The XOR spreads both read patterns (16 rows x 32
+// bytes at one column offset) over all banks.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct TSlotGeo {
+  static_assert(D * (int)sizeof(T) == 256, "sixteen 16-byte units per row");
+  static constexpr int K_BYTES = 64 * 256;
+  static constexpr int T_OFF = K_BYTES, T_BYTES = 64 * 64 * (int)sizeof(T);
+  static constexpr int G_OFF = T_OFF + T_BYTES;
+  static constexpr int R_OFF = G_OFF + 256;       // two rows of 64 floats
+  static constexpr int BYTES = R_OFF + 512;
+  static constexpr int NK = K_BYTES / 1024, NTF = T_BYTES / 1024;
+  static constexpr int NP = NK + NTF + 3;         // loads per chunk (three 256-byte rows)
+};
+
+// Byte offset in a T-form slot of k row r, elements e .. e + 3 (e % 4 == 0).
+__device__ __forceinline__ int tk_off(int r, int e) {
+  return r * 256 + 16 * ((e >> 3) ^ (r & 15)) + 2 * (e & 7);
+}
+
+// Loader wave `part` of NLD for the T form: piece i of a chunk goes to part
+// i % NLD.  k rows past the chunk's last token repeat that token's row (their
+// scales are zero).
+template <typename T, int D, int NLD>
+struct TLoader {
+  using SG = TSlotGeo<T, D>;
+  static constexpr int PPW = (SG::NP + NLD - 1) / NLD;
+  static constexpr int MIN_PER_PART = SG::NP / NLD;
+  int lane, part;
+  const T *k;        // the sequence's first k row of this k head
+  int64_t kstride;   // elements from one token's k row to the next
+
+  __device__ __forceinline__ void issue(const Args &a, int64_t ch, int cc, int len,
+                                        unsigned char *slot) const {
+    const int rows = min(kChunk, len - kChunk * cc);
+    const T *kc = k + (int64_t)kChunk * cc * kstride;
+    const unsigned char *tf = (const unsigned char *)a.Wf + ch * SG::T_BYTES;
+#pragma unroll
+    for (int m = 0; m < PPW; ++m) {
+      const int i = part + NLD * m;
+      if (i < SG::NK) {
+        // LDS unit p of row r holds the row's unit p ^ (r % 16)
+        const int r = 4 * i + (lane >> 4), p = lane & 15;
+        dma16(kc + (int64_t)min(r, rows - 1) * kstride + 8 * (p ^ (r & 15)), slot + i * 1024);
+      } else if (i < SG::NK + SG::NTF) {
+        dma16(tf + (i - SG::NK) * 1024 + 16 * lane, slot + i * 1024);
+      } else if (i == SG::NK + SG::NTF) {
+        dma4(a.Gw + ch * kChunk + lane, slot + SG::G_OFF);
+      } else if (i < SG::NP) {
+        const int row = i - SG::NK - SG::NTF - 1;
+        dma4(a.Bw + ch * 128 + 64 * row + lane, slot + SG::R_OFF + 256 * row);
+      }
+    }
+  }
+};
+
+// One chunk of the recurrence in the T form for one compute wave's 16-column
+// tile (as chunk_step, with the operands of a T-form slot and the tile's U
+// in registers).  The chunk-start state and N (unscaled) go to the output
+// waves through xb.
+template <typename T, int D>
+__device__ __forceinline__ void tform_step(const unsigned char *slot, const T (*u)[4],
+                                           float (&S)[D / 16][4], int lane,
+                                           typename Mfma<T>::frag *xb) {
+  using M = Mfma<T>;
+  using SG = TSlotGeo<T, D>;
+  typedef typename M::frag frag;
+  constexpr int KPL = M::KPL, NT = D / 16, KS_D = D / 32, KS_C = 2;
+  const int g = lane >> 4, c = lane & 15;
+  auto frag2 = [](i16x4 lo, i16x4 hi) {
+    return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // the state as operand fragments (dk in pi order), handed to the output waves
+  const float *Sflat = &S[0][0];
+  frag sb[KS_D];
+#pragma unroll
+  for (int kt = 0; kt < KS_D; ++kt) {
+    sb[kt] = M::pack(Sflat + kt * KPL);
+    xb[kt * 64 + lane] = sb[kt];
+  }
+  // X = K S: A fragments are k rows 16 it + c, dk in pi order (two 8-byte runs)
+  f32x4 x[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) x[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < KS_D; ++kt)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int r = 16 * it + c, e0 = 32 * kt + 4 * g;
+      const i16x4 lo = *reinterpret_cast<const i16x4 *>(slot + tk_off(r, e0));
+      const i16x4 hi = *reinterpret_cast<const i16x4 *>(slot + tk_off(r, e0 + 16));
+      x[it] = M::mma(frag2(lo, hi), sb[kt], x[it]);
+    }
+  // rows 16 it + 4 g + r of X scaled by 1/n, as the T product's B operand
+  // (t in pi order)
+  const float *rs = reinterpret_cast<const float *>(slot + SG::R_OFF);
+  float xf[16];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const f32x4 n4 = *reinterpret_cast<const f32x4 *>(rs + 16 * it + 4 * g);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) xf[4 * it + r] = x[it][r] * n4[r];
+  }
+  frag xt[KS_C];
+#pragma unroll
+  for (int kt = 0; kt < KS_C; ++kt) xt[kt] = M::pack(xf + kt * KPL);
+  // N = U + (-T diag(beta exp G)) X
+  f32x4 acc[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it)
+    acc[it] = f32x4{to_f32(u[it][0]), to_f32(u[it][1]), to_f32(u[it][2]), to_f32(u[it][3])};
+#pragma unroll
+  for (int kt = 0; kt < KS_C; ++kt)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const frag tf = *reinterpret_cast<const frag *>(slot + SG::T_OFF +
+                                                      ((it * KS_C + kt) * 64 + lane) * 16);
+      acc[it] = M::mma(tf, xt[kt], acc[it]);
+    }
+  float accf[16];
+#pragma unroll
+  for (int it = 0; it < 4; ++it)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) accf[4 * it + r] = acc[it][r];
+  frag nf[KS_C];
+#pragma unroll
+  for (int kt = 0; kt < KS_C; ++kt) {
+    nf[kt] = M::pack(accf + kt * KPL);
+    xb[(KS_D + kt) * 64 + lane] = nf[kt];
+  }
+  // N's rows scaled by exp(G_last - G_t) / n_t for the update
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(rs + 64 + 16 * it + 4 * g);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) accf[4 * it + r] *= b4[r];
+  }
+#pragma unroll
+  for (int kt = 0; kt < KS_C; ++kt) nf[kt] = M::pack(accf + kt * KPL);
+  // S' = exp(G_last) S + K^T (scaled N): A fragments (dk rows 16 it + c, t in
+  // pi order) through transposed reads of the k rows
+  const float gl = gexp(reinterpret_cast<const float *>(slot + SG::G_OFF)[kChunk - 1]);
+#pragma unroll
+  for (int it = 0; it < NT; ++it) {
+    f32x4 s4 = {S[it][0] * gl, S[it][1] * gl, S[it][2] * gl, S[it][3] * gl};
+#pragma unroll
+    for (int kt = 0; kt < KS_C; ++kt) {
+      const int r0 = 32 * kt + 4 * g + (c >> 2), col = 16 * it + 4 * (c & 3);
+      const i16x4 lo = lds_read_tr4(reinterpret_cast<const T *>(slot + tk_off(r0, col)));
+      const i16x4 hi = lds_read_tr4(reinterpret_cast<const T *>(slot + tk_off(r0 + 16, col)));
+      s4 = M::mma(frag2(lo, hi), nf[kt], s4);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S[it][r] = s4[r];
+  }
+}
+
+
 // One output wave's operands for one chunk: q fragments of its two token
 // tiles, the unmasked P fragments (one for the first tile, two for the
 // second) and the gate values of its two rows.
@@ -378,24 +551,31 @@ template <> struct FusedRoles<4> {
 // segment that holds the sequence's last chunk.  Segments past a sequence's
 // end exit at once (segment 0 still runs for an empty sequence, whose final
 // state is its initial state).
-template <typename T, int D, int TW, bool CP = false, bool SHK = false>
+//
+// TF: the T form (four tiles, no context parallelism; see TSlotGeo).  Its
+// slots are smaller, so four fit and the loaders run two chunks ahead.
+template <typename T, int D, int TW, bool CP = false, bool SHK = false, bool TF = false>
 __global__ void __launch_bounds__(64 * FusedRoles<TW>::kWaves)
 state_output_kernel(Args a) {
   using R = FusedRoles<TW>;
-  constexpr int NT = D / 16, NWG = NT / TW, NLD = kFusedLoadWaves, NSLOT = R::kSlots;
+  static_assert(!TF || (TW == 4 && !CP), "the T form is a four-tile pass without segments");
+  constexpr int NT = D / 16, NWG = NT / TW, NLD = kFusedLoadWaves, NSLOT = TF ? 4 : R::kSlots;
   constexpr int AHEAD = NSLOT - 2;     // chunks the loaders run ahead
   // four tiles: the slots hold W, Ktilde and the gate row, and each compute
   // wave fetches its U tile into registers (LDS holds three such slots and
   // the four tiles' double-buffered hand-off)
   constexpr bool UREG = TW >= 4;
-  using SG = DmaSlotGeo<T, D, UREG ? 0 : TW>;
-  using LD = DmaLoader<T, D, NLD, UREG ? 0 : TW>;
+  using SGW = DmaSlotGeo<T, D, UREG ? 0 : TW>;
+  using LDW = DmaLoader<T, D, NLD, UREG ? 0 : TW>;
+  using SLT = std::conditional_t<TF, TSlotGeo<T, D>, SGW>;
+  using LDT = std::conditional_t<TF, TLoader<T, D, NLD>, LDW>;
+  constexpr int LD_MIN = LDT::MIN_PER_PART;
   typedef typename Mfma<T>::frag frag;
   constexpr int XB = Geo<T, D>::KS_D + Geo<T, D>::KS_C;  // fragments per chunk in xbuf
   static_assert(AHEAD == 1 || AHEAD == 2, "the loader waits below handle one or two chunks ahead");
-  static_assert(AHEAD * LD::MIN_PER_PART <= 63, "vmcnt range");
+  static_assert(AHEAD * LD_MIN <= 63, "vmcnt range");
   static_assert(NT % TW == 0, "whole tiles per workgroup");
-  __shared__ __align__(16) unsigned char cslots[NSLOT][SG::BYTES];
+  __shared__ __align__(16) unsigned char cslots[NSLOT][SLT::BYTES];
   __shared__ frag xbuf[TW][2][XB * 64];
   __shared__ __align__(16) unsigned char junk[256];
 
@@ -479,12 +659,16 @@ state_output_kernel(Args a) {
         fill.load(a, ch0 + (int64_t)min(st, nc - 1), jg, lane);
         lds_sync();
         const int cc = st - 1;
-        SlotRegUOps<T, D, SHK> op;
-        op.slot = cslots[cc % NSLOT];
-        op.lane = lane;
-        op.utile = 0;
-        op.u = use.u;
-        chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[ct][cc & 1]);
+        if constexpr (TF) {
+          tform_step<T, D>(cslots[cc % NSLOT], use.u, S, lane, xbuf[ct][cc & 1]);
+        } else {
+          SlotRegUOps<T, D, SHK> op;
+          op.slot = cslots[cc % NSLOT];
+          op.lane = lane;
+          op.utile = 0;
+          op.u = use.u;
+          chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[ct][cc & 1]);
+        }
         checkpoint(cc);
       };
       if (nc > 0) u0.load(a, ch0, jg, lane);
@@ -546,18 +730,28 @@ state_output_kernel(Args a) {
     wait_vm<0>();
   } else if (part >= 0) {
     // ---------------- loader waves ------------------------------------------
-    const LD ld{(int64_t)jg0 * (SG::U_TILE_BYTES / 16), lane, part, k_block(a, ch0, h) - ch0};
-    for (int cc = 0; cc < AHEAD && cc < nc; ++cc) ld.issue(a, ch0 + (int64_t)cc, cslots[cc]);
+    LDT ld;
+    if constexpr (TF) {
+      const int kh = h / (H / a.hk);
+      ld = LDT{lane, part, (const T *)a.k + ((int64_t)sbos * a.hk + kh) * D, (int64_t)a.hk * D};
+    } else {
+      ld = LDT{(int64_t)jg0 * (SGW::U_TILE_BYTES / 16), lane, part, k_block(a, ch0, h) - ch0};
+    }
+    auto issue = [&](int cc) {
+      if constexpr (TF) ld.issue(a, ch0 + (int64_t)cc, cc, len, cslots[cc % NSLOT]);
+      else ld.issue(a, ch0 + (int64_t)cc, cslots[cc % NSLOT]);
+    };
+    for (int cc = 0; cc < AHEAD && cc < nc; ++cc) issue(cc);
     for (int st = 0; st <= nc + 1; ++st) {
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-      if (st + AHEAD < nc) ld.issue(a, ch0 + (int64_t)(st + AHEAD), cslots[(st + AHEAD) % NSLOT]);
+      if (st + AHEAD < nc) issue(st + AHEAD);
       // chunk st must have landed before the next barrier; the loads issued
       // after it (up to AHEAD newer chunks where they exist) may stay in flight
       if (st < nc) {
         const int newer = min(AHEAD, nc - 1 - st);
-        if (newer >= 2) wait_vm<2 * LD::MIN_PER_PART>();
-        else if (newer == 1) wait_vm<LD::MIN_PER_PART>();
+        if (newer >= 2) wait_vm<2 * LD_MIN>();
+        else if (newer == 1) wait_vm<LD_MIN>();
         else wait_vm<0>();
       }
     }
@@ -567,7 +761,7 @@ state_output_kernel(Args a) {
   }
 }
 
-template <typename T, int D, int TW>
+template <typename T, int D, int TW, bool TF = false>
 static hipError_t launch_state_output_tw(const Args &a, hipStream_t s) {
   constexpr int NWG = D / 16 / TW;
   const bool cp = a.cp_nseg > 0;
@@ -581,6 +775,12 @@ static hipError_t launch_state_output_tw(const Args &a, hipStream_t s) {
   }
   const dim3 grid((unsigned)blocks), block(64 * FusedRoles<TW>::kWaves);
   const bool shk = a.H != a.hk;   // sab heads share k heads (GQA / GVA)
+  if constexpr (TF) {
+    if (cp) return hipErrorInvalidValue;
+    if (shk) state_output_kernel<T, D, TW, false, true, true><<<grid, block, 0, s>>>(a);
+    else state_output_kernel<T, D, TW, false, false, true><<<grid, block, 0, s>>>(a);
+    return hipGetLastError();
+  }
   if constexpr (D == 128) {
     if (cp) {
       if (shk) state_output_kernel<T, D, TW, true, true><<<grid, block, 0, s>>>(a);
@@ -607,6 +807,12 @@ static hipError_t launch_state_output_t(const Args &a, hipStream_t s) {
   // the four-tile grid covers every CU: the operand traffic per column halves
   // again.
   const int64_t cus = a.num_cus > 0 ? a.num_cus : 1;
+  // the T form (chosen by the host with the intra-chunk pass's output form)
+  if constexpr (D == 128) {
+    if (a.tform) return launch_state_output_tw<T, D, 4, true>(a, s);
+  } else {
+    if (a.tform) return hipErrorInvalidValue;
+  }
   if constexpr (NT % 4 == 0) {
     if (units * NT >= 4 * cus) return launch_state_output_tw<T, D, 4>(a, s);
   }

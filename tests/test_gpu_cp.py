@@ -137,14 +137,14 @@ def cp_workspace_offsets(T, N, H, D, nseg, hq=None, hk=None):
     """Byte offsets of the context-parallel buffers in a 16-bit call's
     workspace (the layout of gdn_prefill_workspace_size: chunk tables, then
     W, the k fragments (per k head), U, the q fragments (per q head), P,
-    gates, then the segment start states, local states and transitions, each
-    256-byte aligned)."""
+    gates, the T form's row scales, then the segment start states, local
+    states and transitions, each 256-byte aligned)."""
     cap = int(nat.lib().gdn_max_chunks(T, N))
     blocks = cap * H
     kb, qb = cap * (hk or H), cap * (hq or H)
     sizes = [8 * max(cap, 1), 8 * max(cap, 1), 4 * (N + 1), 4 * (N + 1), 4,
              blocks * 64 * D * 2, kb * 64 * D * 2, blocks * 64 * D * 2,
-             qb * 64 * D * 2, blocks * 64 * 64 * 2, blocks * 64 * 4]
+             qb * 64 * D * 2, blocks * 64 * 64 * 2, blocks * 64 * 4, blocks * 128 * 4]
     off = 0
     for sz in sizes:
         off = _align(off + sz)

@@ -1,0 +1,96 @@
+"""GPU parity of the four-tile state pass in its T form, through the C ABI.
+
+Batches with at least four 16-column state tiles per CU at D = 128 (16-bit,
+without context parallelism) take the fused pass with four tiles per
+workgroup, in the T form: the intra-chunk pass stores T diag(beta exp(G))
+(T = (I + A)^-1) instead of W, and the state pass forms
+W S = T diag(beta exp(G)) diag(1/|k|) (K S) and
+Ktilde^T N = K^T diag(exp(G_last - G) / |k|) N from the raw k rows
+(0539edu "GDN与线性注意力GPU并行实现", section 3.2: W and U are T applied to
+the decayed keys and the values, so the product with the state can take T
+last; weigao.cc "GDN 与 Chunked Prefill", the WY form).  The oracle's token
+recurrence is still the definition.  The cases cover ragged lengths with
+empty, one-token and chunk-boundary sequences, checkpoints, in-place pools,
+shared q/k heads, fp16, narrow states and inputs normalised outside the
+kernel.
+"""
+import numpy as np
+import pytest
+
+from gated_deltanet_chunked_varlen_amd import workloads as W
+from tests import gdn_testlib as tl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def _four_tiles(wl):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return wl.D == 128 and wl.N * wl.H * (wl.D // 16) >= 4 * cus
+
+
+def _lengths(seed, n, hi):
+    rng = np.random.default_rng(seed)
+    lengths = [int(x) for x in rng.integers(1, hi, size=n)]
+    lengths[:6] = [0, 1, 64, 65, 127, 128]
+    return lengths
+
+
+def _check(wl, gpu, orc):
+    errs, _ = tl.compare(wl, gpu, orc)
+    bars = tl.bars(wl)
+    print(wl.name, {k: "%.3e" % v for k, v in errs.items()}, "bars", bars, flush=True)
+    for k, e in errs.items():
+        assert e <= bars[k], (k, e, bars[k])
+
+
+CASES = {
+    "bf16_equal_heads_ckpt": dict(heads=(8, 8, 8), dtype="bf16", l2norm_in_kernel=True,
+                                  init="seq", checkpoint_every=128),
+    "f16_equal_heads": dict(heads=(8, 8, 8), dtype="f16", l2norm_in_kernel=True, init="seq",
+                            init_dtype="f16", final_state_dtype="f16"),
+    "bf16_gva_pool": dict(heads=(4, 4, 8), dtype="bf16", l2norm_in_kernel=True, init="pool",
+                          pool_size=70, in_place_pool=True),
+    "bf16_gqa_norm_outside": dict(heads=(8, 2, 2), dtype="bf16", normalise_in_generator=True,
+                                  init="seq", checkpoint_every=64, checkpoint_dtype="bf16"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_tform_four_tile_pass(case):
+    kw = dict(CASES[case])
+    hq, hk, hv = kw.pop("heads")
+    dtype = kw.pop("dtype")
+    seed = 60 + sorted(CASES).index(case)
+    H = max(hq, hk, hv)
+    n = -(-1024 // (8 * H)) + 3
+    wl = W.make(seed, _lengths(seed, n, 300), hq, hk, hv, 128, dtype, name="tform_" + case,
+                init_std=0.3, **kw)
+    assert _four_tiles(wl)
+    gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] == 0
+    _check(wl, gpu, tl.run_oracle(wl))
+    if kw.get("in_place_pool"):
+        rows = set(int(r) for r in wl.state_indices)
+        others = [r for r in range(kw["pool_size"]) if r not in rows]
+        np.testing.assert_array_equal(gpu["final"][others], gpu["pool_before"][others])
+
+
+def test_tform_long_sequences_large_keys():
+    # unnormalised keys of norm ~45 (normalised in the kernel) and long
+    # sequences: the raw k rows enter K S unscaled, 1/|k| is applied after
+    wl = W.make(66, [3000, 2500] + [200] * 14, 8, 8, 8, 128, "bf16", l2norm_in_kernel=True,
+                init="seq", init_std=0.3, name="tform_large_keys")
+    wl.k = wl.k * 4.0          # a power of two: still exact in bf16
+    assert _four_tiles(wl)
+    gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] == 0
+    _check(wl, gpu, tl.run_oracle(wl))
