@@ -341,7 +341,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
     const T *vrow = (const T *)a.v + ((bos + lt) * a.hv + vh) * D;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-      vraw[i] = valid ? *reinterpret_cast<const u32x4 *>(vrow + 32 * i + 8 * lp) : u32x4{0, 0, 0, 0};
+      vraw[i] = (valid && !TF) ? *reinterpret_cast<const u32x4 *>(vrow + 32 * i + 8 * lp)
+                               : u32x4{0, 0, 0, 0};
     frag kn[NV];
     float kinv;
     load_norm_row16<T, D>((const T *)a.k + ((bos + lt) * a.hk + kh) * D, lp, valid,
@@ -514,12 +515,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
 
   const int w = wave;  // token tile of this wave
   if constexpr (TF) {
-    // ---- T form: -T diag(beta exp(G)) and the row scales ---------------------
-    // The state pass forms W S = T diag(beta exp(G)) diag(1/|k|) (K S) from
-    // the raw k rows, so instead of -W this stores the 64 x 64 factor as
-    // operand fragments: [w][kt][lane] = rows 16 w + c, columns (tokens) in
-    // pi order, matching the pi order of K S's result rows; and per token
-    // 1/|k_t| and exp(G_last - G_t) / |k_t| (Ktilde^T N = K^T diag(that) N).
+    // ---- T form: -T diag(beta) and the row scales ----------------------------
+    // The state pass forms N = U - W S = T diag(beta) (V - diag(exp(G) / |k|)
+    // (K S)) from the raw k and v rows, so instead of -W and U this stores
+    // the 64 x 64 factor -T diag(beta) as operand fragments: [w][kt][lane] =
+    // rows 16 w + c, columns (tokens) in pi order, matching the pi order of
+    // the products' result rows; and per token exp(G_t) / |k_t| and
+    // exp(G_last - G_t) / |k_t| (Ktilde^T N = K^T diag(that) N).  v is not
+    // read here at all.
     T *tf = (T *)a.Wf + ch * (int64_t)(64 * 64) + (int64_t)w * KS_C * 64 * 8;
 #pragma unroll
     for (int kt = 0; kt < KS_C; ++kt) {
@@ -527,16 +530,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = 32 * kt + 16 * (e >> 2) + 4 * g + (e & 3);
-        y[e] = -AT[16 * w + c][j] * AT[j][65] * gexp(AT[j][64]);
+        y[e] = -AT[16 * w + c][j] * AT[j][65];
       }
       st_inter<NTS>(reinterpret_cast<frag *>(tf + ((int64_t)kt * 64 + lane) * 8), M::pack(y));
     }
     if (wave == 0) {
-      const float inv = AT[lane][66];
+      const float inv = AT[lane][66], gt = AT[lane][64];
       float *bw = a.Bw + ch * 128;
-      bw[lane] = inv;
-      bw[64 + lane] = gexp(AT[63][64] - AT[lane][64]) * inv;
+      bw[lane] = gexp(gt) * inv;
+      bw[64 + lane] = gexp(AT[63][64] - gt) * inv;
     }
+    return;
   } else {
   // ---- W (as W^T tiles): A operand = k columns via transposed reads --------
   {

@@ -221,91 +221,110 @@ struct UTile {
 
 // ---------------------------------------------------------------------------
 // T form of the four-tile pass (16-bit, D = 128).  With S the chunk-start
-// state, K the chunk's raw k rows, n_t = |k_t| (1 without normalisation) and
-// T = (I + A)^-1 from the intra-chunk pass:
+// state, K and V the chunk's raw k and v rows, n_t = |k_t| (1 without
+// normalisation) and T = (I + A)^-1 from the intra-chunk pass, U = T
+// diag(beta) V and W = T diag(beta exp(G)) diag(1/n) K, so
 //
-//   W S          = T diag(beta exp(G)) diag(1/n) (K S)
+//   N            = U - W S = (-T diag(beta)) (diag(exp(G) / n) (K S) - V)
 //   Ktilde^T N   = K^T diag(exp(G_last - G) / n) N
 //
-// so the slot holds the raw k rows (read twice: as rows for K S, and through
-// transposed reads for K^T) and the 64 x 64 factor -T diag(beta exp(G))
-// instead of -W and Ktilde^T: 24 KB of operands per chunk instead of 32, and
-// the intra-chunk pass writes 8 KB per chunk-head instead of -W and Ktilde^T
-// (16 KB each).  The k rows come straight from the input (shared by the sab
-// heads of a k head).  A slot: [k rows, 16-byte units of row r permuted by
-// XOR with r mod 16][-T diag(beta exp G) fragments][gate row][1/n row]
-// [exp(G_last - G)/n row].  The XOR spreads both read patterns (16 rows x 32
-// bytes at one column offset) over all banks.
+// and the slot holds the raw k rows (read twice: as rows for K S, and through
+// transposed reads for K^T), the workgroup's 64 columns of the raw v rows
+// and the 64 x 64 factor -T diag(beta) instead of -W, Ktilde^T and U.  The
+// intra-chunk pass then writes 8 KB per chunk-head instead of -W, U (16 KB
+// each) and Ktilde^T, and reads no v.  k and v come straight from the input
+// (k shared by the sab heads of a k head).  A slot: [k rows][v rows][-T
+// diag(beta) fragments][gate row][exp(G)/n row][exp(G_last - G)/n row].  The
+// 16-byte units of each k row are permuted by XOR with (row mod 16), those of
+// each 128-byte v row with (row / 2 mod 8), so every read pattern below (16
+// rows x 32 bytes at one column offset) spreads over all banks.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, int TW>
 struct TSlotGeo {
-  static_assert(D * (int)sizeof(T) == 256, "sixteen 16-byte units per row");
+  static_assert(D * (int)sizeof(T) == 256 && TW == 4,
+                "sixteen 16-byte units per k row, eight per v row");
   static constexpr int K_BYTES = 64 * 256;
-  static constexpr int T_OFF = K_BYTES, T_BYTES = 64 * 64 * (int)sizeof(T);
+  static constexpr int V_OFF = K_BYTES, V_BYTES = 64 * TW * 16 * (int)sizeof(T);
+  static constexpr int T_OFF = V_OFF + V_BYTES, T_BYTES = 64 * 64 * (int)sizeof(T);
   static constexpr int G_OFF = T_OFF + T_BYTES;
   static constexpr int R_OFF = G_OFF + 256;       // two rows of 64 floats
   static constexpr int BYTES = R_OFF + 512;
-  static constexpr int NK = K_BYTES / 1024, NTF = T_BYTES / 1024;
-  static constexpr int NP = NK + NTF + 3;         // loads per chunk (three 256-byte rows)
+  static constexpr int NK = K_BYTES / 1024, NV = V_BYTES / 1024, NTF = T_BYTES / 1024;
+  static constexpr int NP = NK + NV + NTF + 3;    // loads per chunk (three 256-byte rows)
 };
 
-// Byte offset in a T-form slot of k row r, elements e .. e + 3 (e % 4 == 0).
+// Byte offsets in a T-form slot of k row r, elements e .. e + 3, and of v
+// row r, slot columns e .. e + 3 (e % 4 == 0).
 __device__ __forceinline__ int tk_off(int r, int e) {
   return r * 256 + 16 * ((e >> 3) ^ (r & 15)) + 2 * (e & 7);
 }
+__device__ __forceinline__ int tv_off(int r, int e) {
+  return 64 * 256 + r * 128 + 16 * ((e >> 3) ^ ((r >> 1) & 7)) + 2 * (e & 7);
+}
 
 // Loader wave `part` of NLD for the T form: piece i of a chunk goes to part
-// i % NLD.  k rows past the chunk's last token repeat that token's row (their
-// scales are zero).
-template <typename T, int D, int NLD>
+// i % NLD.  k and v rows past the chunk's last token repeat that token's rows
+// (their scales and factor columns are zero).
+template <typename T, int D, int NLD, int TW>
 struct TLoader {
-  using SG = TSlotGeo<T, D>;
+  using SG = TSlotGeo<T, D, TW>;
   static constexpr int PPW = (SG::NP + NLD - 1) / NLD;
   static constexpr int MIN_PER_PART = SG::NP / NLD;
   int lane, part;
-  const T *k;        // the sequence's first k row of this k head
-  int64_t kstride;   // elements from one token's k row to the next
+  const T *k, *v;    // the sequence's first k row of this k head; v row, first column
+  int64_t kstride, vstride;  // elements from one token's row to the next
 
   __device__ __forceinline__ void issue(const Args &a, int64_t ch, int cc, int len,
                                         unsigned char *slot) const {
     const int rows = min(kChunk, len - kChunk * cc);
     const T *kc = k + (int64_t)kChunk * cc * kstride;
+    const T *vc = v + (int64_t)kChunk * cc * vstride;
     const unsigned char *tf = (const unsigned char *)a.Wf + ch * SG::T_BYTES;
 #pragma unroll
     for (int m = 0; m < PPW; ++m) {
       const int i = part + NLD * m;
       if (i < SG::NK) {
-        // LDS unit p of row r holds the row's unit p ^ (r % 16)
+        // LDS unit p of k row r holds the row's unit p ^ (r % 16)
         const int r = 4 * i + (lane >> 4), p = lane & 15;
         dma16(kc + (int64_t)min(r, rows - 1) * kstride + 8 * (p ^ (r & 15)), slot + i * 1024);
-      } else if (i < SG::NK + SG::NTF) {
-        dma16(tf + (i - SG::NK) * 1024 + 16 * lane, slot + i * 1024);
-      } else if (i == SG::NK + SG::NTF) {
+      } else if (i < SG::NK + SG::NV) {
+        // LDS unit p of v row r holds the row's unit p ^ (r / 2 % 8)
+        const int r = 8 * (i - SG::NK) + (lane >> 3), p = lane & 7;
+        dma16(vc + (int64_t)min(r, rows - 1) * vstride + 8 * (p ^ ((r >> 1) & 7)), slot + i * 1024);
+      } else if (i < SG::NK + SG::NV + SG::NTF) {
+        dma16(tf + (i - SG::NK - SG::NV) * 1024 + 16 * lane, slot + i * 1024);
+      } else if (i == SG::NK + SG::NV + SG::NTF) {
         dma4(a.Gw + ch * kChunk + lane, slot + SG::G_OFF);
       } else if (i < SG::NP) {
-        const int row = i - SG::NK - SG::NTF - 1;
+        const int row = i - SG::NK - SG::NV - SG::NTF - 1;
         dma4(a.Bw + ch * 128 + 64 * row + lane, slot + SG::R_OFF + 256 * row);
       }
     }
   }
 };
 
-// One chunk of the recurrence in the T form for one compute wave's 16-column
-// tile (as chunk_step, with the operands of a T-form slot and the tile's U
-// in registers).  The chunk-start state and N (unscaled) go to the output
-// waves through xb.
-template <typename T, int D>
-__device__ __forceinline__ void tform_step(const unsigned char *slot, const T (*u)[4],
+// One chunk of the recurrence in the T form for compute wave ct's 16-column
+// tile (as chunk_step, with the operands of a T-form slot).  The chunk-start
+// state and N (unscaled) go to the output waves through xb.
+template <typename T, int D, int TW>
+__device__ __forceinline__ void tform_step(const unsigned char *slot, int ct,
                                            float (&S)[D / 16][4], int lane,
                                            typename Mfma<T>::frag *xb) {
   using M = Mfma<T>;
-  using SG = TSlotGeo<T, D>;
+  using SG = TSlotGeo<T, D, TW>;
   typedef typename M::frag frag;
   constexpr int KPL = M::KPL, NT = D / 16, KS_D = D / 32, KS_C = 2;
   const int g = lane >> 4, c = lane & 15;
   auto frag2 = [](i16x4 lo, i16x4 hi) {
     return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
+  // v rows 16 it + 4 g .. + 3 of this tile's column c (result layout), by
+  // transposed reads; independent of the state, so read first
+  i16x4 v4[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it)
+    v4[it] = lds_read_tr4(reinterpret_cast<const T *>(slot + tv_off(16 * it + 4 * g + (c >> 2),
+                                                                     16 * ct + 4 * (c & 3))));
   // the state as operand fragments (dk in pi order), handed to the output waves
   const float *Sflat = &S[0][0];
   frag sb[KS_D];
@@ -327,31 +346,31 @@ __device__ __forceinline__ void tform_step(const unsigned char *slot, const T (*
       const i16x4 hi = *reinterpret_cast<const i16x4 *>(slot + tk_off(r, e0 + 16));
       x[it] = M::mma(frag2(lo, hi), sb[kt], x[it]);
     }
-  // rows 16 it + 4 g + r of X scaled by 1/n, as the T product's B operand
-  // (t in pi order)
+  // Y = diag(exp(G) / n) X - V (rows 16 it + 4 g + r), as the B operand of
+  // the T product (t in pi order)
   const float *rs = reinterpret_cast<const float *>(slot + SG::R_OFF);
-  float xf[16];
+  float yf[16];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const f32x4 n4 = *reinterpret_cast<const f32x4 *>(rs + 16 * it + 4 * g);
+    const f32x4 a4 = *reinterpret_cast<const f32x4 *>(rs + 16 * it + 4 * g);
+    const auto vv = __builtin_bit_cast(typename M::half, v4[it]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) xf[4 * it + r] = x[it][r] * n4[r];
+    for (int r = 0; r < 4; ++r) yf[4 * it + r] = x[it][r] * a4[r] - to_f32(vv[r]);
   }
-  frag xt[KS_C];
+  frag yt[KS_C];
 #pragma unroll
-  for (int kt = 0; kt < KS_C; ++kt) xt[kt] = M::pack(xf + kt * KPL);
-  // N = U + (-T diag(beta exp G)) X
+  for (int kt = 0; kt < KS_C; ++kt) yt[kt] = M::pack(yf + kt * KPL);
+  // N = (-T diag(beta)) Y
   f32x4 acc[4];
 #pragma unroll
-  for (int it = 0; it < 4; ++it)
-    acc[it] = f32x4{to_f32(u[it][0]), to_f32(u[it][1]), to_f32(u[it][2]), to_f32(u[it][3])};
+  for (int it = 0; it < 4; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kt = 0; kt < KS_C; ++kt)
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const frag tf = *reinterpret_cast<const frag *>(slot + SG::T_OFF +
                                                       ((it * KS_C + kt) * 64 + lane) * 16);
-      acc[it] = M::mma(tf, xt[kt], acc[it]);
+      acc[it] = M::mma(tf, yt[kt], acc[it]);
     }
   float accf[16];
 #pragma unroll
@@ -553,22 +572,22 @@ template <> struct FusedRoles<4> {
 // state is its initial state).
 //
 // TF: the T form (four tiles, no context parallelism; see TSlotGeo).  Its
-// slots are smaller, so four fit and the loaders run two chunks ahead.
+// slots hold the v rows too, so the compute waves fetch no U.
 template <typename T, int D, int TW, bool CP = false, bool SHK = false, bool TF = false>
 __global__ void __launch_bounds__(64 * FusedRoles<TW>::kWaves)
 state_output_kernel(Args a) {
   using R = FusedRoles<TW>;
   static_assert(!TF || (TW == 4 && !CP), "the T form is a four-tile pass without segments");
-  constexpr int NT = D / 16, NWG = NT / TW, NLD = kFusedLoadWaves, NSLOT = TF ? 4 : R::kSlots;
+  constexpr int NT = D / 16, NWG = NT / TW, NLD = kFusedLoadWaves, NSLOT = R::kSlots;
   constexpr int AHEAD = NSLOT - 2;     // chunks the loaders run ahead
   // four tiles: the slots hold W, Ktilde and the gate row, and each compute
   // wave fetches its U tile into registers (LDS holds three such slots and
   // the four tiles' double-buffered hand-off)
-  constexpr bool UREG = TW >= 4;
+  constexpr bool UREG = TW >= 4 && !TF;
   using SGW = DmaSlotGeo<T, D, UREG ? 0 : TW>;
   using LDW = DmaLoader<T, D, NLD, UREG ? 0 : TW>;
-  using SLT = std::conditional_t<TF, TSlotGeo<T, D>, SGW>;
-  using LDT = std::conditional_t<TF, TLoader<T, D, NLD>, LDW>;
+  using SLT = std::conditional_t<TF, TSlotGeo<T, D, TW>, SGW>;
+  using LDT = std::conditional_t<TF, TLoader<T, D, NLD, TW>, LDW>;
   constexpr int LD_MIN = LDT::MIN_PER_PART;
   typedef typename Mfma<T>::frag frag;
   constexpr int XB = Geo<T, D>::KS_D + Geo<T, D>::KS_C;  // fragments per chunk in xbuf
@@ -659,16 +678,12 @@ state_output_kernel(Args a) {
         fill.load(a, ch0 + (int64_t)min(st, nc - 1), jg, lane);
         lds_sync();
         const int cc = st - 1;
-        if constexpr (TF) {
-          tform_step<T, D>(cslots[cc % NSLOT], use.u, S, lane, xbuf[ct][cc & 1]);
-        } else {
-          SlotRegUOps<T, D, SHK> op;
-          op.slot = cslots[cc % NSLOT];
-          op.lane = lane;
-          op.utile = 0;
-          op.u = use.u;
-          chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[ct][cc & 1]);
-        }
+        SlotRegUOps<T, D, SHK> op;
+        op.slot = cslots[cc % NSLOT];
+        op.lane = lane;
+        op.utile = 0;
+        op.u = use.u;
+        chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[ct][cc & 1]);
         checkpoint(cc);
       };
       if (nc > 0) u0.load(a, ch0, jg, lane);
@@ -687,8 +702,12 @@ state_output_kernel(Args a) {
         lds_sync();
         if (st == 0 || st > nc) continue;
         const int cc = st - 1;
-        const DmaSlotOps<T, D, TW, SHK> op{cslots[cc % NSLOT], lane, ct};
-        chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[ct][cc & 1]);
+        if constexpr (TF) {
+          tform_step<T, D, TW>(cslots[cc % NSLOT], ct, S, lane, xbuf[ct][cc & 1]);
+        } else {
+          const DmaSlotOps<T, D, TW, SHK> op{cslots[cc % NSLOT], lane, ct};
+          chunk_step<T, D>(a, op, S, ch0 + (int64_t)cc, jg, lane, xbuf[ct][cc & 1]);
+        }
         checkpoint(cc);
       }
     }
@@ -732,8 +751,10 @@ state_output_kernel(Args a) {
     // ---------------- loader waves ------------------------------------------
     LDT ld;
     if constexpr (TF) {
-      const int kh = h / (H / a.hk);
-      ld = LDT{lane, part, (const T *)a.k + ((int64_t)sbos * a.hk + kh) * D, (int64_t)a.hk * D};
+      const int kh = h / (H / a.hk), vh = h / (H / a.hv);
+      ld = LDT{lane, part, (const T *)a.k + ((int64_t)sbos * a.hk + kh) * D,
+               (const T *)a.v + ((int64_t)sbos * a.hv + vh) * D + 16 * jg0,
+               (int64_t)a.hk * D, (int64_t)a.hv * D};
     } else {
       ld = LDT{(int64_t)jg0 * (SGW::U_TILE_BYTES / 16), lane, part, k_block(a, ch0, h) - ch0};
     }
