@@ -369,18 +369,22 @@ static void fill_args(const gdn_prefill_params *p, const Layout *L, int num_cus,
                              (int64_t)(p->num_k_heads + p->num_q_heads) * 64 * D) * 2;
       a.warm = inter > kWarmBytes ? 2 : 0;
       a.nt_stores = inter > kWarmBytes ? 1 : 0;
+      // the state pass in its T form (16-bit D = 128 without context
+      // parallelism) where its extra chain work pays: with two or four tiles
+      // per workgroup (the CU's memory path bounds the step), or where the
+      // intermediates would outgrow the last-level cache (the intra-chunk
+      // pass's traffic halves).  Small one-tile calls are bound by the chain
+      // and keep -W, Ktilde^T and U (2 x 2048 tokens x 16 heads: 52.7 us per
+      // call against 60.6 in the T form; 262 144 tokens x 32 heads: 7.12 ms
+      // against 6.42).
+      const int64_t tiles = (int64_t)p->num_seqs * H * (D / 16);
+      a.tform = (D == 128 && L->cp.nseg == 0 && (tiles > num_cus || inter > kWarmBytes)) ? 1 : 0;
     } else {
       a.Hf = ws + L->Hf;
       a.Nf = ws + L->Nf;
     }
     a.Gw = (float *)(ws + L->Gw);
-    if (L->fuse) {
-      a.Bw = (float *)(ws + L->Bw);
-      // the four-tile state pass (at least four column tiles per CU) in its
-      // T form: 16-bit D = 128 without context parallelism
-      const int64_t tiles = (int64_t)p->num_seqs * H * (D / 16);
-      a.tform = (D == 128 && L->cp.nseg == 0 && num_cus > 0 && tiles >= 4ll * num_cus) ? 1 : 0;
-    }
+    if (L->fuse) a.Bw = (float *)(ws + L->Bw);
     if (L->cp.nseg > 0) {
       a.cp_seg = L->cp.seg;
       a.cp_nseg = L->cp.nseg;

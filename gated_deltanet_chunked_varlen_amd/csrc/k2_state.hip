@@ -236,31 +236,35 @@ struct UTile {
 // (k shared by the sab heads of a k head).  A slot: [k rows][v rows][-T
 // diag(beta) fragments][gate row][exp(G)/n row][exp(G_last - G)/n row].  The
 // 16-byte units of each k row are permuted by XOR with (row mod 16), those of
-// each 128-byte v row with (row / 2 mod 8), so every read pattern below (16
-// rows x 32 bytes at one column offset) spreads over all banks.
+// each v row (TW 32-byte tiles, 2 TW units) with (row / (8 / TW) mod 2 TW),
+// so every read pattern below (16 rows x 32 bytes at one column offset)
+// spreads evenly over the banks.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int TW>
 struct TSlotGeo {
-  static_assert(D * (int)sizeof(T) == 256 && TW == 4,
-                "sixteen 16-byte units per k row, eight per v row");
+  static_assert(D * (int)sizeof(T) == 256, "sixteen 16-byte units per k row");
   static constexpr int K_BYTES = 64 * 256;
-  static constexpr int V_OFF = K_BYTES, V_BYTES = 64 * TW * 16 * (int)sizeof(T);
+  static constexpr int VROW = TW * 16 * (int)sizeof(T), VU = VROW / 16;   // v row bytes, units
+  static constexpr int V_OFF = K_BYTES, V_BYTES = 64 * VROW;
   static constexpr int T_OFF = V_OFF + V_BYTES, T_BYTES = 64 * 64 * (int)sizeof(T);
   static constexpr int G_OFF = T_OFF + T_BYTES;
   static constexpr int R_OFF = G_OFF + 256;       // two rows of 64 floats
   static constexpr int BYTES = R_OFF + 512;
   static constexpr int NK = K_BYTES / 1024, NV = V_BYTES / 1024, NTF = T_BYTES / 1024;
   static constexpr int NP = NK + NV + NTF + 3;    // loads per chunk (three 256-byte rows)
-};
 
-// Byte offsets in a T-form slot of k row r, elements e .. e + 3, and of v
-// row r, slot columns e .. e + 3 (e % 4 == 0).
-__device__ __forceinline__ int tk_off(int r, int e) {
-  return r * 256 + 16 * ((e >> 3) ^ (r & 15)) + 2 * (e & 7);
-}
-__device__ __forceinline__ int tv_off(int r, int e) {
-  return 64 * 256 + r * 128 + 16 * ((e >> 3) ^ ((r >> 1) & 7)) + 2 * (e & 7);
-}
+  // v row r's unit permutation: rows that share banks (256 / VROW of them
+  // apart) get different units
+  __device__ __forceinline__ static int vswz(int r) { return (r / (256 / VROW)) % VU; }
+  // byte offsets in the slot of k row r, elements e .. e + 3, and of v row
+  // r, slot columns e .. e + 3 (e % 4 == 0)
+  __device__ __forceinline__ static int k_off(int r, int e) {
+    return r * 256 + 16 * ((e >> 3) ^ (r & 15)) + 2 * (e & 7);
+  }
+  __device__ __forceinline__ static int v_off(int r, int e) {
+    return V_OFF + r * VROW + 16 * ((e >> 3) ^ vswz(r)) + 2 * (e & 7);
+  }
+};
 
 // Loader wave `part` of NLD for the T form: piece i of a chunk goes to part
 // i % NLD.  k and v rows past the chunk's last token repeat that token's rows
@@ -288,9 +292,9 @@ struct TLoader {
         const int r = 4 * i + (lane >> 4), p = lane & 15;
         dma16(kc + (int64_t)min(r, rows - 1) * kstride + 8 * (p ^ (r & 15)), slot + i * 1024);
       } else if (i < SG::NK + SG::NV) {
-        // LDS unit p of v row r holds the row's unit p ^ (r / 2 % 8)
-        const int r = 8 * (i - SG::NK) + (lane >> 3), p = lane & 7;
-        dma16(vc + (int64_t)min(r, rows - 1) * vstride + 8 * (p ^ ((r >> 1) & 7)), slot + i * 1024);
+        // LDS unit p of v row r holds the row's unit p ^ vswz(r)
+        const int r = (1024 / SG::VROW) * (i - SG::NK) + lane / SG::VU, p = lane % SG::VU;
+        dma16(vc + (int64_t)min(r, rows - 1) * vstride + 8 * (p ^ SG::vswz(r)), slot + i * 1024);
       } else if (i < SG::NK + SG::NV + SG::NTF) {
         dma16(tf + (i - SG::NK - SG::NV) * 1024 + 16 * lane, slot + i * 1024);
       } else if (i == SG::NK + SG::NV + SG::NTF) {
@@ -318,13 +322,31 @@ __device__ __forceinline__ void tform_step(const unsigned char *slot, int ct,
   auto frag2 = [](i16x4 lo, i16x4 hi) {
     return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
+  // With one or two tiles per workgroup (the chain bounds the step) operand
+  // reads are issued ahead of the products that use them, so that their
+  // latency overlaps earlier products: the k rows of K S up front, the
+  // factor's fragments and the row scales during K S, the k columns of K^T
+  // during the factor's product (the state does not enter any of them).
+  // With four tiles the compiler's own order measured faster (0.198 against
+  // 0.203 ms for the GVA batch's state pass).
+  constexpr bool early = TW < 4;
+  // k rows 16 it + c, dk in pi order (two 8-byte runs): A operands of K S
+  frag kr[4][KS_D];
+#pragma unroll
+  for (int kt = 0; kt < KS_D; ++kt)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int r = 16 * it + c, e0 = 32 * kt + 4 * g;
+      kr[it][kt] = frag2(*reinterpret_cast<const i16x4 *>(slot + SG::k_off(r, e0)),
+                         *reinterpret_cast<const i16x4 *>(slot + SG::k_off(r, e0 + 16)));
+    }
   // v rows 16 it + 4 g .. + 3 of this tile's column c (result layout), by
-  // transposed reads; independent of the state, so read first
+  // transposed reads
   i16x4 v4[4];
 #pragma unroll
   for (int it = 0; it < 4; ++it)
-    v4[it] = lds_read_tr4(reinterpret_cast<const T *>(slot + tv_off(16 * it + 4 * g + (c >> 2),
-                                                                     16 * ct + 4 * (c & 3))));
+    v4[it] = lds_read_tr4(reinterpret_cast<const T *>(slot + SG::v_off(16 * it + 4 * g + (c >> 2),
+                                                                         16 * ct + 4 * (c & 3))));
   // the state as operand fragments (dk in pi order), handed to the output waves
   const float *Sflat = &S[0][0];
   frag sb[KS_D];
@@ -333,45 +355,78 @@ __device__ __forceinline__ void tform_step(const unsigned char *slot, int ct,
     sb[kt] = M::pack(Sflat + kt * KPL);
     xb[kt * 64 + lane] = sb[kt];
   }
-  // X = K S: A fragments are k rows 16 it + c, dk in pi order (two 8-byte runs)
+  if constexpr (early) __builtin_amdgcn_sched_barrier(0);
+  // X = K S, with the factor's fragments read meanwhile
   f32x4 x[4];
 #pragma unroll
   for (int it = 0; it < 4; ++it) x[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kt = 0; kt < KS_D; ++kt)
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int r = 16 * it + c, e0 = 32 * kt + 4 * g;
-      const i16x4 lo = *reinterpret_cast<const i16x4 *>(slot + tk_off(r, e0));
-      const i16x4 hi = *reinterpret_cast<const i16x4 *>(slot + tk_off(r, e0 + 16));
-      x[it] = M::mma(frag2(lo, hi), sb[kt], x[it]);
-    }
-  // Y = diag(exp(G) / n) X - V (rows 16 it + 4 g + r), as the B operand of
-  // the T product (t in pi order)
+    for (int it = 0; it < 4; ++it) x[it] = M::mma(kr[it][kt], sb[kt], x[it]);
+  frag tf[4][KS_C];
+#pragma unroll
+  for (int kt = 0; kt < KS_C; ++kt)
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+      tf[it][kt] = *reinterpret_cast<const frag *>(slot + SG::T_OFF +
+                                                   ((it * KS_C + kt) * 64 + lane) * 16);
+  // rows 16 it + 4 g .. + 3 of exp(G) / n and exp(G_last - G) / n; G_last
   const float *rs = reinterpret_cast<const float *>(slot + SG::R_OFF);
+  f32x4 a4[4], b4[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    a4[it] = *reinterpret_cast<const f32x4 *>(rs + 16 * it + 4 * g);
+    b4[it] = *reinterpret_cast<const f32x4 *>(rs + 64 + 16 * it + 4 * g);
+  }
+  const float glast = reinterpret_cast<const float *>(slot + SG::G_OFF)[kChunk - 1];
+  if constexpr (early) {
+#pragma unroll
+    for (int i = 0; i < 4 * KS_C; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two products
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Y = diag(exp(G) / n) X - V (rows 16 it + 4 g + r), as the B operand of
+  // the factor's product (t in pi order)
   float yf[16];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const f32x4 a4 = *reinterpret_cast<const f32x4 *>(rs + 16 * it + 4 * g);
     const auto vv = __builtin_bit_cast(typename M::half, v4[it]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) yf[4 * it + r] = x[it][r] * a4[r] - to_f32(vv[r]);
+    for (int r = 0; r < 4; ++r) yf[4 * it + r] = x[it][r] * a4[it][r] - to_f32(vv[r]);
   }
   frag yt[KS_C];
 #pragma unroll
   for (int kt = 0; kt < KS_C; ++kt) yt[kt] = M::pack(yf + kt * KPL);
-  // N = (-T diag(beta)) Y
+  // N = (-T diag(beta)) Y, with the k columns of K^T (dk rows 16 it + c, t in
+  // pi order) read meanwhile through transposed reads
   f32x4 acc[4];
 #pragma unroll
   for (int it = 0; it < 4; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kt = 0; kt < KS_C; ++kt)
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const frag tf = *reinterpret_cast<const frag *>(slot + SG::T_OFF +
-                                                      ((it * KS_C + kt) * 64 + lane) * 16);
-      acc[it] = M::mma(tf, yt[kt], acc[it]);
+    for (int it = 0; it < 4; ++it) acc[it] = M::mma(tf[it][kt], yt[kt], acc[it]);
+  frag kc[NT][KS_C];
+#pragma unroll
+  for (int it = 0; it < NT; ++it)
+#pragma unroll
+    for (int kt = 0; kt < KS_C; ++kt) {
+      const int r0 = 32 * kt + 4 * g + (c >> 2), col = 16 * it + 4 * (c & 3);
+      kc[it][kt] = frag2(lds_read_tr4(reinterpret_cast<const T *>(slot + SG::k_off(r0, col))),
+                         lds_read_tr4(reinterpret_cast<const T *>(slot + SG::k_off(r0 + 16, col))));
     }
+  if constexpr (early) {
+#pragma unroll
+    for (int i = 0; i < 4 * KS_C; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // four LDS reads
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
   float accf[16];
 #pragma unroll
   for (int it = 0; it < 4; ++it)
@@ -385,26 +440,18 @@ __device__ __forceinline__ void tform_step(const unsigned char *slot, int ct,
   }
   // N's rows scaled by exp(G_last - G_t) / n_t for the update
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(rs + 64 + 16 * it + 4 * g);
+  for (int it = 0; it < 4; ++it)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) accf[4 * it + r] *= b4[r];
-  }
+    for (int r = 0; r < 4; ++r) accf[4 * it + r] *= b4[it][r];
 #pragma unroll
   for (int kt = 0; kt < KS_C; ++kt) nf[kt] = M::pack(accf + kt * KPL);
-  // S' = exp(G_last) S + K^T (scaled N): A fragments (dk rows 16 it + c, t in
-  // pi order) through transposed reads of the k rows
-  const float gl = gexp(reinterpret_cast<const float *>(slot + SG::G_OFF)[kChunk - 1]);
+  // S' = exp(G_last) S + K^T (scaled N)
+  const float gl = gexp(glast);
 #pragma unroll
   for (int it = 0; it < NT; ++it) {
     f32x4 s4 = {S[it][0] * gl, S[it][1] * gl, S[it][2] * gl, S[it][3] * gl};
 #pragma unroll
-    for (int kt = 0; kt < KS_C; ++kt) {
-      const int r0 = 32 * kt + 4 * g + (c >> 2), col = 16 * it + 4 * (c & 3);
-      const i16x4 lo = lds_read_tr4(reinterpret_cast<const T *>(slot + tk_off(r0, col)));
-      const i16x4 hi = lds_read_tr4(reinterpret_cast<const T *>(slot + tk_off(r0 + 16, col)));
-      s4 = M::mma(frag2(lo, hi), nf[kt], s4);
-    }
+    for (int kt = 0; kt < KS_C; ++kt) s4 = M::mma(kc[it][kt], nf[kt], s4);
 #pragma unroll
     for (int r = 0; r < 4; ++r) S[it][r] = s4[r];
   }
@@ -577,7 +624,7 @@ template <typename T, int D, int TW, bool CP = false, bool SHK = false, bool TF 
 __global__ void __launch_bounds__(64 * FusedRoles<TW>::kWaves)
 state_output_kernel(Args a) {
   using R = FusedRoles<TW>;
-  static_assert(!TF || (TW == 4 && !CP), "the T form is a four-tile pass without segments");
+  static_assert(!TF || !CP, "the T form runs without segments");
   constexpr int NT = D / 16, NWG = NT / TW, NLD = kFusedLoadWaves, NSLOT = R::kSlots;
   constexpr int AHEAD = NSLOT - 2;     // chunks the loaders run ahead
   // four tiles: the slots hold W, Ktilde and the gate row, and each compute
@@ -738,7 +785,7 @@ state_output_kernel(Args a) {
       ++st;
     }
     if (st < nc + 2) output_wave_step<T, D, TW>(a, st, nc, len, sbos, ch0, jg0, h, lane, ow, r0, r1, xbuf);
-  } else if (wave == R::warm_wave(hbm)) {
+  } else if (!TF && wave == R::warm_wave(hbm)) {
     // ---------------- L2 warm-up wave ---------------------------------------
     const int ahead = a.warm;
     for (int cc = 0; cc < ahead && cc < nc; ++cc) L2Warm<T, D, TW>::touch(a, ch0 + cc, h, jw, lane, junk);
@@ -828,16 +875,21 @@ static hipError_t launch_state_output_t(const Args &a, hipStream_t s) {
   // the four-tile grid covers every CU: the operand traffic per column halves
   // again.
   const int64_t cus = a.num_cus > 0 ? a.num_cus : 1;
+  const int tw = (NT % 4 == 0 && units * NT >= 4 * cus) ? 4 : units * NT > cus ? 2 : 1;
   // the T form (chosen by the host with the intra-chunk pass's output form)
   if constexpr (D == 128) {
-    if (a.tform) return launch_state_output_tw<T, D, 4, true>(a, s);
+    if (a.tform) {
+      if (tw == 4) return launch_state_output_tw<T, D, 4, true>(a, s);
+      if (tw == 2) return launch_state_output_tw<T, D, 2, true>(a, s);
+      return launch_state_output_tw<T, D, 1, true>(a, s);
+    }
   } else {
     if (a.tform) return hipErrorInvalidValue;
   }
   if constexpr (NT % 4 == 0) {
-    if (units * NT >= 4 * cus) return launch_state_output_tw<T, D, 4>(a, s);
+    if (tw == 4) return launch_state_output_tw<T, D, 4>(a, s);
   }
-  if (units * NT > cus) return launch_state_output_tw<T, D, 2>(a, s);
+  if (tw == 2) return launch_state_output_tw<T, D, 2>(a, s);
   return launch_state_output_tw<T, D, 1>(a, s);
 }
 

@@ -1,18 +1,19 @@
-"""GPU parity of the four-tile state pass in its T form, through the C ABI.
+"""GPU parity of the state pass in its T form, through the C ABI.
 
-Batches with at least four 16-column state tiles per CU at D = 128 (16-bit,
-without context parallelism) take the fused pass with four tiles per
-workgroup, in the T form: the intra-chunk pass stores T diag(beta exp(G))
-(T = (I + A)^-1) instead of W, and the state pass forms
-W S = T diag(beta exp(G)) diag(1/|k|) (K S) and
-Ktilde^T N = K^T diag(exp(G_last - G) / |k|) N from the raw k rows
+16-bit calls at D = 128 without context parallelism take the T form where
+the state pass runs two or four 16-column tiles per workgroup, or where the
+intermediates outgrow the last-level cache: the intra-chunk pass stores
+-T diag(beta) (T = (I + A)^-1) and two row scales instead of -W, Ktilde^T
+and U, and the state pass forms N = U - W S =
+(-T diag(beta)) (diag(exp(G) / |k|) (K S) - V) and
+Ktilde^T N = K^T diag(exp(G_last - G) / |k|) N from the raw k and v rows
 (0539edu "GDN与线性注意力GPU并行实现", section 3.2: W and U are T applied to
-the decayed keys and the values, so the product with the state can take T
-last; weigao.cc "GDN 与 Chunked Prefill", the WY form).  The oracle's token
-recurrence is still the definition.  The cases cover ragged lengths with
-empty, one-token and chunk-boundary sequences, checkpoints, in-place pools,
-shared q/k heads, fp16, narrow states and inputs normalised outside the
-kernel.
+the decayed keys and the values, so the products can take T last; weigao.cc
+"GDN 与 Chunked Prefill", the WY form).  The oracle's token recurrence is
+still the definition.  The cases cover four, two and one tile per workgroup,
+ragged lengths with empty, one-token and chunk-boundary sequences,
+checkpoints, in-place pools, shared q/k heads, fp16, narrow states and inputs
+normalised outside the kernel.
 """
 import numpy as np
 import pytest
@@ -32,9 +33,13 @@ def _gpu():
     yield
 
 
-def _four_tiles(wl):
+def _tiles_per_cu(wl):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    return wl.D == 128 and wl.N * wl.H * (wl.D // 16) >= 4 * cus
+    return wl.N * wl.H * (wl.D // 16) / cus
+
+
+def _four_tiles(wl):
+    return wl.D == 128 and _tiles_per_cu(wl) >= 4
 
 
 def _lengths(seed, n, hi):
@@ -92,5 +97,26 @@ def test_tform_long_sequences_large_keys():
     wl.k = wl.k * 4.0          # a power of two: still exact in bf16
     assert _four_tiles(wl)
     gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] == 0
+    _check(wl, gpu, tl.run_oracle(wl))
+
+
+def test_tform_two_tile_pass():
+    # between one and four tiles per CU: two tiles per workgroup
+    wl = W.make(67, _lengths(67, 10, 400), 8, 8, 8, 128, "bf16", l2norm_in_kernel=True,
+                init="pool", pool_size=23, in_place_pool=True, init_std=0.3,
+                checkpoint_every=192, name="tform_two_tiles")
+    assert 1 < _tiles_per_cu(wl) < 4
+    gpu = tl.run_gpu(wl, status=True)
+    assert gpu["status"] == 0
+    _check(wl, gpu, tl.run_oracle(wl))
+
+
+def test_tform_one_tile_pass_large_call():
+    # one 65 536-token sequence with four heads without context parallelism:
+    # one tile per workgroup, intermediates past the last-level cache
+    wl = W.long_l65536_h4_d128()
+    assert _tiles_per_cu(wl) <= 1
+    gpu = tl.run_gpu(wl, status=True, use_cp=False)
     assert gpu["status"] == 0
     _check(wl, gpu, tl.run_oracle(wl))
