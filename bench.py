@@ -61,11 +61,11 @@ KERNEL_SOURCES = {
 COMMON_SOURCES = ("gdn_common.h", "gdn_internal.h", "gdn_state.h")
 
 
-def per_token_head_bytes(wl, phase):
+def per_token_head_bytes(wl, phase, tform=False):
     """Algorithmic HBM bytes per (token, sab head) of each phase (fp32 gates,
     q/k/v/o and intermediates in the compute dtype of width e).
 
-    16-bit inputs (the state pass forms the output itself):
+    16-bit inputs (the state pass forms the output itself), W form:
       intra : reads q, k, v, g, beta; writes W and U (64 x D each per
               chunk-head), the normalised k and q fragments (64 x D per chunk
               and k / q head), the six unmasked 16 x 32 blocks of the masked
@@ -73,6 +73,12 @@ def per_token_head_bytes(wl, phase):
               gates
       state : reads W, the k fragments, U, the q fragments, those Q K^T
               blocks and the gates; writes o
+    16-bit inputs, T form (tform):
+      intra : reads q, k, g, beta; writes -T diag(beta) (64 x 64 per
+              chunk-head), the q fragments, the Q K^T blocks, the gates and
+              two rows of scales
+      state : reads k, v, -T diag(beta), the q fragments, the Q K^T blocks,
+              the gates and the scales; writes o
     fp32 inputs (separate output pass):
       intra : reads k, v, g, beta; writes W, Ktilde, U and the gates
       state : reads W, Ktilde, U, G_last; writes the chunk-start state
@@ -84,6 +90,13 @@ def per_token_head_bytes(wl, phase):
     e = 4 if wl.dtype == "f32" else 2
     hq, hk, hv = wl.q.shape[1], wl.k.shape[1], wl.v.shape[1]
     qf, kf, vf = hq / H, hk / H, hv / H
+    if wl.dtype != "f32" and tform:
+        inter = 64 * e + qf * D * e + 48 * e + 4 + 8
+        if phase == "intra":
+            return (qf + kf) * D * e + 8 + inter
+        if phase == "state":
+            return inter + (kf + vf) * D * e + D * e
+        return 0.0
     if wl.dtype != "f32":
         inter = (2 + kf + qf) * D * e + 48 * e + 4
         if phase == "intra":
@@ -518,6 +531,8 @@ def measure_prefill(wl, steps, warmup, cold_calls, use_cp="auto"):
     need = api.workspace_size(p)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     p.workspace, p.workspace_bytes = ctypes.c_void_p(ws.data_ptr()), need
+    form = state_form(wl, need != api.workspace_size(api.make_params(
+        d["q"], d["k"], d["v"], use_cp=False, **kw)[0]))
     lib = nat.lib()
     L = hip()
     stream = torch.cuda.current_stream().cuda_stream
@@ -609,7 +624,26 @@ def measure_prefill(wl, steps, warmup, cold_calls, use_cp="auto"):
                 "flush_read_bytes": 512 << 20, "calls": cold_calls}
 
     return dict(wl=wl, ms_total=ms_total, K=K, wall=wall, phase_ms=phase_ms, dom=dom,
-                dom_ms=dom_ms, cold=cold)
+                dom_ms=dom_ms, cold=cold, form=form)
+
+
+def state_form(wl, cp):
+    """The state pass's operand form for this call, as the library chooses it
+    (for the implementation byte model only): context parallelism (cp, seen
+    from the workspace size), else the T form for 16-bit D = 128 calls with
+    more column tiles than CUs or W-form intermediates past 200 MiB."""
+    import torch
+    from gated_deltanet_chunked_varlen_amd import _native as nat
+    if cp:
+        return "context parallel (W form)"
+    if wl.dtype == "f32" or wl.D != 128:
+        return "W form"
+    H, D = wl.H, wl.D
+    hq, hk = wl.q.shape[1], wl.k.shape[1]
+    cap = int(nat.lib().gdn_max_chunks(wl.T, wl.N))
+    inter = cap * (H * (2 * 64 * D + 64 * 64) + (hk + hq) * 64 * D) * 2
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return "T form" if (wl.N * H * (D // 16) > cus or inter > (200 << 20)) else "W form"
 
 
 def prefill_record(m):
@@ -636,7 +670,7 @@ def prefill_record(m):
     peak_mm = FP32_PEAK_TFLOPS if wl.dtype == "f32" else BF16_PEAK_TFLOPS   # fp16 peak = bf16 peak
     mbytes = method_bytes(wl)
     achieved = mbytes / (dom_ms / 1e3) / 1e9
-    impl_bytes = per_token_head_bytes(wl, dom) * T * H
+    impl_bytes = per_token_head_bytes(wl, dom, m["form"] == "T form") * T * H
     traffic = load_traffic(dom, wl.name)
     return {
         "ms_per_step": ms_step,
@@ -646,6 +680,7 @@ def prefill_record(m):
         "mfma_peak_frac": tflops / peak_mm,
         "phase_ms_warmup": phase_ms,
         "mfma_counters": load_mfma(wl.name) or None,
+        "state_pass_form": m["form"],
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "traffic_source": TRAFFIC_SOURCE if traffic else None,
