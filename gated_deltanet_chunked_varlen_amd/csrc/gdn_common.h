@@ -274,29 +274,15 @@ __device__ __forceinline__ void load_row_part(const Tin *row, int p, float (&x)[
 // see the same k rows.  inv (optional) receives the factor applied: the
 // row's inverse norm, or 1 without normalisation.
 template <typename T, int D>
-__device__ __forceinline__ void norm_row16(const u32x4 (&raw)[D / 32], bool l2norm,
-                                           typename Mfma<T>::frag (&out)[D / 32],
-                                           float *inv_out = nullptr);
-
-template <typename T, int D>
 __device__ __forceinline__ void load_norm_row16(const T *row, int p, bool valid, bool l2norm,
                                                 typename Mfma<T>::frag (&out)[D / 32],
                                                 float *inv_out = nullptr) {
+  typedef typename Mfma<T>::frag frag;
   constexpr int NV = D / 32;
   u32x4 raw[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i)
     raw[i] = valid ? *reinterpret_cast<const u32x4 *>(row + 32 * i + 8 * p) : u32x4{0, 0, 0, 0};
-  norm_row16<T, D>(raw, l2norm, out, inv_out);
-}
-
-// The normalisation of load_norm_row16 for a row part already in registers.
-template <typename T, int D>
-__device__ __forceinline__ void norm_row16(const u32x4 (&raw)[D / 32], bool l2norm,
-                                           typename Mfma<T>::frag (&out)[D / 32],
-                                           float *inv_out) {
-  typedef typename Mfma<T>::frag frag;
-  constexpr int NV = D / 32;
   if (!l2norm) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) out[i] = __builtin_bit_cast(frag, raw[i]);
