@@ -17,6 +17,9 @@ Three independent forms of the same definition live here:
 * ``exact_token`` -- the same recurrence in exact rational arithmetic
   (``fractions.Fraction``), for tiny sizes such as L = 8, D = 8, the first run
   0539edu "GDN与线性注意力GPU并行实现" section 3.1 recommends.
+* ``chunk_factors`` -- one chunk's WY factors (A, T = (I + A)^-1, W, U) in
+  numpy from the chunked form's definition, for checks of the GPU path's
+  stored intermediates.
 * ``partial_transition`` -- the pair-composition form of 0539edu sections
   2.1-2.2: each position is an affine pair ``(A_i, B_i)`` with
   ``A_i = a_i (I - b_i k_i k_i^T)``, ``B_i = b_i k_i v_i^T``; inside a chunk an
@@ -252,6 +255,41 @@ def chunked(p: Problem, C: int = 64, dump: bool = False) -> dict:
         raise RuntimeError("oracle_gdn_chunked failed: %d" % rc)
     return {"out": out, "final": final, "ckpt": ck, "chunk_states": cs,
             "vnew": vn}
+
+
+def chunk_factors(p: Problem, h: int, t0: int, n: int) -> dict:
+    """The WY factors of one chunk (tokens t0 .. t0 + n - 1 of one sequence)
+    for sab head h, in fp64 (weigao.cc "GDN 与 Chunked Prefill", section
+    "递推公式如何展开成块内计算"; 0539edu "GDN与线性注意力GPU并行实现",
+    section 3.2).  With the gate log-cumsum inside the chunk
+    G_t = sum_{s <= t} ln alpha_s, the keys k_t (L2-normalised when
+    ``p.l2norm``, norm n_t; n_t = 1 otherwise) and beta_t:
+
+        A[t, j] = beta_t exp(G_t - G_j) k_t . k_j   for j < t, else 0
+        T       = (I + A)^-1
+        W       = T diag(beta exp(G)) K,    U = T diag(beta) V
+
+    and the chunk's new values are U - W S for S the state entering the chunk
+    (as a D_k x D_v matrix).  Returns T, W, U, beta, G and the key norms n.
+    Pinned against the C chunked form's new values (tests/test_oracle_pins.py)."""
+    H = p.H
+    kh = h // (H // p.k.shape[1])
+    vh = h // (H // p.v.shape[1])
+    K = np.asarray(p.k[t0:t0 + n, kh], np.float64)
+    V = np.asarray(p.v[t0:t0 + n, vh], np.float64)
+    if p.l2norm:
+        nk = np.sqrt(np.sum(K * K, axis=1) + 1e-6)
+        K = K / nk[:, None]
+    else:
+        nk = np.ones(n)
+    alpha = np.ones(n) if p.g is None else np.asarray(p.g[t0:t0 + n, h], np.float64)
+    beta = np.ones(n) if p.beta is None else np.asarray(p.beta[t0:t0 + n, h], np.float64)
+    G = np.cumsum(np.log(alpha))
+    A = np.tril(beta[:, None] * np.exp(G[:, None] - G[None, :]) * (K @ K.T), -1)
+    T = np.linalg.inv(np.eye(n) + A)
+    W = T @ ((beta * np.exp(G))[:, None] * K)
+    U = T @ (beta[:, None] * V)
+    return {"T": T, "W": W, "U": U, "beta": beta, "G": G, "knorm": nk}
 
 
 def chunk_table(cu, C: int = 64, cap: Optional[int] = None):

@@ -120,3 +120,100 @@ def test_tform_one_tile_pass_large_call():
     gpu = tl.run_gpu(wl, status=True, use_cp=False)
     assert gpu["status"] == 0
     _check(wl, gpu, tl.run_oracle(wl))
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+def tform_workspace_offsets(T, N, H, D, hq, hk):
+    """Byte offsets of the factor blocks (in the W region) and of the row
+    scales in a 16-bit call's workspace (the layout of
+    gdn_prefill_workspace_size: chunk tables, W, k fragments per k head, U,
+    q fragments per q head, P, gates, row scales, each 256-byte aligned)."""
+    from gated_deltanet_chunked_varlen_amd import _native as nat
+    cap = int(nat.lib().gdn_max_chunks(T, N))
+    blocks = cap * H
+    sizes = [8 * max(cap, 1), 8 * max(cap, 1), 4 * (N + 1), 4 * (N + 1), 4]
+    off = 0
+    for sz in sizes:
+        off = _align(off + sz)
+    wf = off
+    after = [blocks * 64 * D * 2, cap * hk * 64 * D * 2, blocks * 64 * D * 2,
+             cap * hq * 64 * D * 2, blocks * 64 * 64 * 2, blocks * 64 * 4]
+    for sz in after:
+        off = _align(off + sz)
+    return cap, wf, off, _align(off + blocks * 128 * 4)
+
+
+def _decode_factor(block):
+    """[64, 64] from the operand-fragment order: fragment (w, kt), lane
+    16 g + c, slot e holds row 16 w + c, column 32 kt + 16 (e / 4) + 4 g + e % 4."""
+    out = np.zeros((64, 64))
+    b = block.reshape(4, 2, 64, 8)
+    for w in range(4):
+        for kt in range(2):
+            for lane in range(64):
+                g, c = lane // 16, lane % 16
+                for e in range(8):
+                    out[16 * w + c, 32 * kt + 16 * (e // 4) + 4 * g + e % 4] = b[w, kt, lane, e]
+    return out
+
+
+@pytest.mark.parametrize("dtype,l2norm", [("bf16", True), ("f16", False)])
+def test_tform_intermediates_match_oracle_chunk_factors(dtype, l2norm):
+    # 0539edu section 3.1 (compare intermediates step by step): the stored
+    # -T diag(beta) of every chunk and head against oracle.chunk_factors, and
+    # the row scales exp(G) / |k|, exp(G_last - G) / |k| (zero past the end)
+    from gated_deltanet_chunked_varlen_amd import api, chunk_gated_delta_rule
+    from oracle import oracle
+    lengths = [130, 1, 64, 200, 65, 90, 17, 128, 40, 77]
+    kw = dict(l2norm_in_kernel=True) if l2norm else dict(normalise_in_generator=True)
+    wl = W.make(68, lengths, 4, 4, 8, 128, dtype, init="seq", init_std=0.3,
+                name="tform_intermediates", **kw)
+    assert _tiles_per_cu(wl) > 1
+    d = tl.to_device(wl)
+    H, D, N, T = wl.H, wl.D, wl.N, wl.T
+    cap, wf, gw_end, end = tform_workspace_offsets(T, N, H, D, 4, 4)
+    p, _, _ = api.make_params(d["q"], d["k"], d["v"], cu_seqlens=d["cu_seqlens"])
+    assert api.workspace_size(p) == end
+    ws = torch.zeros(end, dtype=torch.uint8, device="cuda")
+    chunk_gated_delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=wl.scale,
+                           cu_seqlens=d["cu_seqlens"], use_qk_l2norm_in_kernel=l2norm,
+                           initial_state=d["initial_state"], workspace=ws)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    prob = oracle.Problem(q=wl.q, k=wl.k, v=wl.v, cu=wl.cu_seqlens.astype(np.int64), g=wl.g,
+                          beta=wl.beta, scale=wl.scale, l2norm=l2norm, init_state=None,
+                          state_indices=None, ckpt_every=0, ckpt_cu_starts=None)
+    table, cc, n = oracle.chunk_table(wl.cu_seqlens, 64)
+    worst_t, worst_r = 0.0, 0.0
+    for f in range(n):
+        i, c = (int(x) for x in table[f])
+        t0 = int(wl.cu_seqlens[i]) + 64 * c
+        m = min(64, int(wl.cu_seqlens[i + 1]) - t0)
+        for h in range(H):
+            ch = h * cap + f
+            b = raw[wf + ch * 8192: wf + (ch + 1) * 8192].view(np.uint16)
+            if dtype == "f16":
+                vals = b.view(np.float16).astype(np.float64)
+            else:
+                vals = (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            got = _decode_factor(vals)
+            fa = oracle.chunk_factors(prob, h, t0, m)
+            want = np.zeros((64, 64))
+            want[:m, :m] = -fa["T"] * fa["beta"][None, :]
+            e = tl.rel_l2(got, want)
+            worst_t = max(worst_t, e)
+            assert e < 2e-2, (f, h, e)
+            rows = raw[gw_end + ch * 512: gw_end + (ch + 1) * 512].view(np.float32).astype(np.float64)
+            G = fa["G"]
+            wa = np.zeros(64)
+            wb = np.zeros(64)
+            wa[:m] = np.exp(G) / fa["knorm"]
+            wb[:m] = np.exp(G[-1] - G) / fa["knorm"]
+            np.testing.assert_allclose(rows[:64], wa, rtol=1e-4, atol=1e-7)
+            np.testing.assert_allclose(rows[64:], wb, rtol=1e-4, atol=1e-7)
+            worst_r = max(worst_r, float(np.max(np.abs(rows[:64] - wa) / np.maximum(np.abs(wa), 1e-30))))
+    print("tform intermediates", dtype, "worst factor rel-L2 %.3e" % worst_t,
+          "worst row rel %.3e" % worst_r, flush=True)

@@ -460,3 +460,37 @@ def test_intermediates_chunk_states_and_new_values():
                 nu = p.beta[t, h] * (p.v[t, h] - p.g[t, h] * Sprev.T @ K[t, h])
                 np.testing.assert_allclose(ch["vnew"][t, h], nu, rtol=1e-10,
                                            atol=1e-12)
+
+
+def test_chunk_factors_reproduce_the_chunked_new_values():
+    """oracle.chunk_factors (numpy, T = (I + A)^-1 by matrix inverse) against
+    the C chunked form (a unit-lower-triangular solve): for every chunk and
+    head, U - W S_chunkstart equals the dumped new values, and T (I + A) = I
+    with T unit lower triangular."""
+    lengths = [150, 64, 10, 129]
+    p = rand_problem(31, lengths, D=8, init=True)
+    ch = oracle.chunked(p, 64, dump=True)
+    table, cc, n = oracle.chunk_table(p.cu, 64)
+    for f in range(n):
+        i, c = (int(x) for x in table[f])
+        t0 = int(p.cu[i]) + 64 * c
+        m = min(64, int(p.cu[i + 1]) - t0)
+        for h in range(p.H):
+            fa = oracle.chunk_factors(p, h, t0, m)
+            S = ch["chunk_states"][f, h].T          # [k][v]
+            np.testing.assert_allclose(fa["U"] - fa["W"] @ S, ch["vnew"][t0:t0 + m, h],
+                                       rtol=1e-9, atol=1e-11)
+            T = fa["T"]
+            assert np.allclose(np.triu(T, 1), 0) and np.allclose(np.diag(T), 1)
+    # a plausible slip (the decay on the wrong side of A) breaks the match
+    p2 = rand_problem(32, [64], D=8, init=True)
+    ch2 = oracle.chunked(p2, 64, dump=True)
+    fa = oracle.chunk_factors(p2, 0, 0, 64)
+    G, beta = fa["G"], fa["beta"]
+    K = p2.k[0:64, 0] / np.sqrt(np.sum(p2.k[0:64, 0] ** 2, 1) + 1e-6)[:, None]
+    A_bad = np.tril(beta[:, None] * np.exp(G[None, :] - G[:, None]) * (K @ K.T), -1)
+    T_bad = np.linalg.inv(np.eye(64) + A_bad)
+    W_bad = T_bad @ ((beta * np.exp(G))[:, None] * K)
+    U_bad = T_bad @ (beta[:, None] * p2.v[0:64, 0])
+    S = ch2["chunk_states"][0, 0].T
+    assert not np.allclose(U_bad - W_bad @ S, ch2["vnew"][0:64, 0], rtol=1e-6)
