@@ -534,6 +534,39 @@ __device__ __forceinline__ void output_regs(const Args &a, const OutRegs<T, D> &
   }
 }
 
+// The output values of one chunk for one 16-column tile (output wave ow),
+// scaled and rounded, without storing them: res[i] for token tile i.
+template <typename T, int D>
+__device__ __forceinline__ void output_values(const Args &a, const OutRegs<T, D> &r,
+                                              const typename Mfma<T>::frag *xb, int lane, int ow,
+                                              typename Mfma<T>::half (&res)[2]) {
+  using M = Mfma<T>;
+  typedef typename M::frag frag;
+  constexpr int KS_D = Geo<T, D>::KS_D, KS_C = Geo<T, D>::KS_C;
+  frag sf[KS_D], nf[KS_C];
+#pragma unroll
+  for (int kt = 0; kt < KS_D; ++kt) sf[kt] = xb[kt * 64 + lane];
+#pragma unroll
+  for (int kt = 0; kt < KS_C; ++kt) nf[kt] = xb[(KS_D + kt) * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < KS_D; ++kt) acc = M::mma(sf[kt], r.q[i][kt], acc);
+    const float gam = gexp(r.g[i]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= gam;
+    if (i == 0) {
+      acc = M::mma(nf[0], r.p0, acc);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < KS_C; ++kt) acc = M::mma(nf[kt], r.p1[kt], acc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) res[i][e] = (T)(a.scale * acc[e]);
+  }
+}
+
 // One step of an output wave (st >= 2): fetch chunk st into `into` (past
 // the last chunk it repeats the last chunk), then output chunk st - 2 from
 // `proc`, fetched two steps earlier, for each of the workgroup's TW column
@@ -550,11 +583,38 @@ __device__ __forceinline__ void output_wave_step(const Args &a, int st, int nc, 
   const int oc = st - 2;
   const int64_t tok0 = (int64_t)sbos + (int64_t)kChunk * oc;
   const int rows = min(kChunk, len - kChunk * oc);
-  if constexpr (TW >= 4) {
-    // one tile at a time (keeps the wave's registers within its share)
-#pragma unroll 1
-    for (int t = 0; t < TW; ++t)
-      output_regs<T, D>(a, proc, xbuf[t][oc & 1], jg0 + t, tok0, rows, h, lane, ow);
+  if constexpr (TW >= 2) {
+    // all tiles' values first, then stores of 16 contiguous bytes per lane:
+    // lanes 16 apart (g, g ^ 1) swap halves so that each holds 8 consecutive
+    // columns of one tile, and one store writes 64 contiguous bytes of each
+    // of 16 rows (two tiles) instead of 32 (GVA batch state pass 0.1995 ->
+    // 0.1878 ms; the output stores had cost it 15 %)
+    typename Mfma<T>::half res[TW][2];
+#pragma unroll
+    for (int t = 0; t < TW; ++t) output_values<T, D>(a, proc, xbuf[t][oc & 1], lane, ow, res[t]);
+    const int g = lane >> 4, c = lane & 15;
+    const bool odd = (g & 1) != 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int tt = i == 0 ? ow : 3 - ow;
+      const int t = 16 * tt + c;
+#pragma unroll
+      for (int pr = 0; pr < TW / 2; ++pr) {
+        const uint2 lo = __builtin_bit_cast(uint2, res[2 * pr][i]);
+        const uint2 hi = __builtin_bit_cast(uint2, res[2 * pr + 1][i]);
+        const uint2 send = odd ? lo : hi;
+        uint2 recv;
+        recv.x = __shfl_xor((int)send.x, 16);
+        recv.y = __shfl_xor((int)send.y, 16);
+        // even g: own tile 2pr columns 4g .. 4g + 3, then the partner's
+        // 4g + 4 .. 4g + 7; odd g: the partner's tile 2pr + 1 columns
+        // 4g - 4 .. 4g - 1, then its own 4g .. 4g + 3
+        const uint4 v = odd ? uint4{recv.x, recv.y, hi.x, hi.y} : uint4{lo.x, lo.y, recv.x, recv.y};
+        const int col = 16 * (jg0 + 2 * pr + (odd ? 1 : 0)) + 4 * (g & 2);
+        if (t < rows)
+          *reinterpret_cast<uint4 *>((T *)a.out + ((tok0 + t) * a.H + h) * D + col) = v;
+      }
+    }
   } else {
 #pragma unroll
     for (int t = 0; t < TW; ++t)
