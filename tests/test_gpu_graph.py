@@ -229,3 +229,33 @@ def test_context_parallel_call_replays_bit_equal_to_eager():
             assert int(s["st"].item()) == 0
             assert torch.equal(got_out, e_out) and torch.equal(got_fin, e_fin), (rnd, seed)
     assert graphs.graphs_captured == 2
+
+
+def test_tform_call_replays_bit_equal_to_eager():
+    # the T form of the four-tile pass (raw k / v rows loaded by the state
+    # pass, no memset) under capture, with rotated buffer sets: each replay
+    # equals an eager call bit for bit
+    lengths = [300, 1, 64, 129, 250, 90, 200, 77, 140, 33, 180, 65, 100, 150, 210, 40]
+    H, D = 8, 128
+    mk = lambda seed: W.make(seed, lengths, H, H, H, D, "bf16", l2norm_in_kernel=True,
+                             init="seq", init_std=0.3)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert len(lengths) * H * (D // 16) >= 4 * cus
+    sets = [_buffer_set(150 + i, lengths, H, D, mk) for i in range(2)]
+    graphs = api.PrefillGraphs()
+    seed = 160
+    for rnd in range(2):
+        for s in sets:
+            _refill(s, mk(seed))
+            seed += 1
+            got_out, got_fin = graphs(s["q"], s["k"], s["v"], s["g"], s["beta"], **_args(s))
+            torch.cuda.synchronize()
+            got_out, got_fin = got_out.clone(), got_fin.clone()
+            e_out, e_fin = chunk_gated_delta_rule(
+                s["q"], s["k"], s["v"], s["g"], s["beta"], initial_state=s["initial_state"],
+                output_final_state=True, cu_seqlens=s["cu_seqlens"],
+                use_qk_l2norm_in_kernel=True)
+            torch.cuda.synchronize()
+            assert int(s["st"].item()) == 0
+            assert torch.equal(got_out, e_out) and torch.equal(got_fin, e_fin), (rnd, seed)
+    assert graphs.graphs_captured == 2
