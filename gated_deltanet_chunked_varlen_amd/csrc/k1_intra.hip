@@ -640,6 +640,238 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
   }
 }
 
+// ---------------------------------------------------------------------------
+// T form where R = H / hk = H / hq sab heads (2 .. 4) share each q and k head
+// (GVA: two v heads per q/k head).  One workgroup per (chunk, q/k head) loads
+// and normalises the q and k rows once and forms the raw Q K^T and K K^T
+// products once; then, for each of its R sab heads in turn, it applies that
+// head's gates and beta (P, A), inverts I + A and stores -T diag(beta) and
+// the row scales, as the one-head T form does.  The q and k loads were half
+// of a one-head workgroup's life.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct IntraSmemS {
+  IntraSmemB<T, D> b;
+  float G[4][64], B[4][64], inv[64];  // per sab head gate log-cumsum, beta; 1/|k|
+};
+
+template <typename T, int D, bool NTS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+intra_tform_shared_kernel(Args a) {
+  using M = Mfma<T>;
+  typedef typename M::frag frag;
+  constexpr int KS_D = D / 32, KS_C = 2, NV = D / 32;
+  constexpr int LDK = IntraSmemB<T, D>::LDK;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  IntraSmemS<T, D> &sm = *reinterpret_cast<IntraSmemS<T, D> *>(smem_raw);
+  float(*AT)[68] = sm.b.AT;
+  T(*KV)[LDK] = sm.b.KV;
+
+  const int H = a.H, R = H / a.hk;
+  const int f = (int)(blockIdx.x / a.hk), kh = (int)(blockIdx.x % a.hk);
+  const int h0 = kh * R;  // first sab head of this q/k head
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tb, len;
+  chunk_geometry(a, f, lane, blockIdx.x == 0 && wave == 0, tb, len);
+  if (len <= 0) return;
+  const int64_t bos = tb;
+  const int g = lane >> 4, c = lane & 15;
+
+  // ---- normalised k rows and q rows into LDS; per-head gates ---------------
+  const int lt = tid >> 2, lp = tid & 3;
+  {
+    const bool valid = lt < len;
+    frag kn[NV], qn[NV];
+    float kinv;
+    load_norm_row16<T, D>((const T *)a.k + ((bos + lt) * a.hk + kh) * D, lp, valid,
+                          a.l2norm != 0, kn, &kinv);
+    load_norm_row16<T, D>((const T *)a.q + ((bos + lt) * a.hq + kh) * D, lp, valid,
+                          a.l2norm != 0, qn);
+    // q rows in the A/T buffer until the first head's A is formed
+    T *qrow = reinterpret_cast<T *>(&AT[lt][0]);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      *reinterpret_cast<frag *>(&KV[lt][32 * i + 8 * lp]) = kn[i];
+      *reinterpret_cast<frag *>(qrow + 32 * i + 8 * lp) = qn[i];
+    }
+    if (lp == 0) sm.inv[lt] = valid ? kinv : 0.f;
+  }
+  if (wave < R) {
+    // wave r: gate log-cumsum and beta of sab head h0 + r
+    const int h = h0 + wave, t = lane;
+    const bool valid = t < len;
+    float la = 0.f, be = 0.f;
+    if (valid) {
+      const int64_t gi = (bos + t) * H + h;
+      la = a.g ? logf(a.g[gi]) : 0.f;
+      be = a.beta ? a.beta[gi] : 1.f;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(la, o);
+      if (lane >= o) la += y;
+    }
+    sm.G[wave][t] = la;
+    sm.B[wave][t] = be;
+    a.Gw[ws_index(f, h, a.cap) * kChunk + t] = la;
+  }
+  lds_sync();
+
+  // ---- raw Q K^T (token tile tt = wave) and K K^T (row tile it = wave) -----
+  const int tt = wave, it = wave;
+  f32x4 qk[4], kk[4];
+  {
+    const T(*QR)[136] = reinterpret_cast<const T(*)[136]>(&AT[0][0]);
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      qk[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      kk[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (jt <= tt) {
+#pragma unroll
+        for (int kt = 0; kt < KS_D; ++kt) {
+          const int k0 = kt * 32 + g * 8;
+          const frag fk = *reinterpret_cast<const frag *>(&KV[16 * jt + c][k0]);
+          qk[jt] = M::mma(fk, *reinterpret_cast<const frag *>(&QR[16 * tt + c][k0]), qk[jt]);
+          kk[jt] = M::mma(*reinterpret_cast<const frag *>(&KV[16 * it + c][k0]), fk, kk[jt]);
+        }
+      }
+    }
+    // q fragments, once for the q head
+    T *qf_out = (T *)a.Qf + q_block(a, ws_index(f, h0, a.cap), h0) * (int64_t)(64 * D);
+    const int t = 16 * tt + c;
+#pragma unroll
+    for (int kt = 0; kt < KS_D; ++kt) {
+      frag qf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[e] = QR[t][pi_idx(g, kt * 8 + e)];
+      st_inter<NTS>(reinterpret_cast<frag *>(qf_out + (((int64_t)tt * KS_D + kt) * 64 + lane) * 8), qf);
+    }
+  }
+
+  for (int r = 0; r < R; ++r) {
+    const int h = h0 + r;
+    const int64_t ch = ws_index(f, h, a.cap);
+    const float *Gr = sm.G[r], *Br = sm.B[r];
+    // ---- P of this head: (Q K^T) masked to j <= t, scaled exp(G_t - G_j) ---
+    {
+      T *pf_out = (T *)a.Pf + ch * (int64_t)(64 * 64);
+      frag pf[KS_C];
+      const int t = 16 * tt + c;
+      const float gt = Gr[t];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * jt + 4 * g + e;
+          const float pv = (j <= t) ? qk[jt][e] * gexp(gt - Gr[j]) : 0.f;
+          const int sl = 4 * jt + e;
+          pf[sl / 8][sl % 8] = (T)pv;
+        }
+#pragma unroll
+      for (int kt = 0; kt < KS_C; ++kt)
+        if (2 * kt <= tt)
+          st_inter<NTS>(reinterpret_cast<frag *>(pf_out + (((int64_t)tt * KS_C + kt) * 64 + lane) * 8), pf[kt]);
+    }
+    lds_sync();  // the q rows (first head) or the previous head's T are consumed
+    // ---- A = strictly-lower(beta_t exp(G_t - G_j) k_t.k_j) ------------------
+    {
+      float Gt[4], Bt[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Gt[e] = Gr[16 * it + 4 * g + e];
+        Bt[e] = Br[16 * it + 4 * g + e];
+      }
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int j = 16 * jt + c;
+        const float Gj = Gr[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * it + 4 * g + e;
+          AT[t][j] = (j < t) ? Bt[e] * gexp(Gt[e] - Gj) * kk[jt][e] : 0.f;
+        }
+      }
+    }
+    lds_sync();
+    // ---- T diagonal blocks (forward substitution, lane c = column c) --------
+    {
+      const int bw = wave;
+      float tc[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float sacc = (i == c) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) sacc = fmaf(-AT[16 * bw + i][16 * bw + m], tc[m], sacc);
+        tc[i] = (i < c) ? 0.f : sacc;
+      }
+      if (g == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) AT[16 * bw + i][16 * bw + c] = tc[i];
+      }
+    }
+    lds_sync();
+    // ---- off-diagonal blocks, one row block at a time ----------------------
+#pragma unroll
+    for (int bi = 1; bi < 4; ++bi) {
+      const int bj = wave;
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      if (bj < bi) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        for (int m = bj; m < bi; ++m) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+            x = Mfma<float>::mma(AT[16 * bi + c][16 * m + 4 * kt + g],
+                                 AT[16 * m + 4 * kt + g][16 * bj + c], x);
+        }
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          y = Mfma<float>::mma(AT[16 * bi + c][16 * bi + 4 * g + kt], x[kt], y);
+      }
+      lds_sync();
+      if (bj < bi) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) AT[16 * bi + 4 * g + e][16 * bj + c] = -y[e];
+      }
+      lds_sync();
+    }
+    // ---- -T diag(beta) (rows 16 w + c, columns in pi order) and row scales --
+    {
+      const int w = wave;
+      T *tf = (T *)a.Wf + ch * (int64_t)(64 * 64) + (int64_t)w * KS_C * 64 * 8;
+#pragma unroll
+      for (int kt = 0; kt < KS_C; ++kt) {
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 32 * kt + 16 * (e >> 2) + 4 * g + (e & 3);
+          y[e] = -AT[16 * w + c][j] * Br[j];
+        }
+        st_inter<NTS>(reinterpret_cast<frag *>(tf + ((int64_t)kt * 64 + lane) * 8), M::pack(y));
+      }
+      if (wave == 0) {
+        const float inv = sm.inv[lane], gt = Gr[lane];
+        float *bw = a.Bw + ch * 128;
+        bw[lane] = gexp(gt) * inv;
+        bw[64 + lane] = gexp(Gr[63] - gt) * inv;
+      }
+    }
+  }
+}
+
+template <typename T, int D, bool NTS>
+static hipError_t launch_intra_tform_shared(const Args &a, hipStream_t s) {
+  const size_t smem = sizeof(IntraSmemS<T, D>);
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = set_dynamic_lds((const void *)intra_tform_shared_kernel<T, D, NTS>, (int)smem, lds_set);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t blocks = a.cap * a.hk;
+  if (blocks == 0) return hipSuccess;
+  intra_tform_shared_kernel<T, D, NTS><<<dim3((unsigned)blocks), dim3(256), smem, s>>>(a);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool NTS, bool SHK, bool TF = false>
 static hipError_t launch_intra_h_nt(const Args &a, hipStream_t s) {
   const size_t smem = sizeof(IntraSmemB<T, D>);
@@ -659,6 +891,11 @@ static hipError_t launch_intra_h(const Args &a, hipStream_t s) {
   // T form (four-tile state pass, D = 128): K^T is not stored, so sab heads
   // sharing k heads need no variant of their own
   if constexpr (D == 128) {
+    // q and k heads both shared by 2 .. 4 sab heads: one workgroup per q/k head
+    const int R = a.H / a.hk;
+    if (a.tform && R >= 2 && R <= 4 && a.hq == a.hk)
+      return a.nt_stores ? launch_intra_tform_shared<T, D, true>(a, s)
+                         : launch_intra_tform_shared<T, D, false>(a, s);
     if (a.tform)
       return a.nt_stores ? launch_intra_h_nt<T, D, true, false, true>(a, s)
                          : launch_intra_h_nt<T, D, false, false, true>(a, s);
