@@ -268,7 +268,8 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
-PROF_KERNELS = {"chunk_index": ("chunk_index_kernel",), "intra": ("intra_kernel", "intra_kernel_h"),
+PROF_KERNELS = {"chunk_index": ("chunk_index_kernel",),
+                "intra": ("intra_kernel", "intra_kernel_h", "intra_tform_shared_kernel"),
                 "state": ("state_kernel", "state_output_kernel", "cp_transition_kernel",
                           "cp_fixup_kernel"),
                 "output": ("output_kernel",), "decode": ("decode_kernel",)}
