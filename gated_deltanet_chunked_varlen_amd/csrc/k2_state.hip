@@ -602,14 +602,15 @@ __device__ __forceinline__ void output_wave_step(const Args &a, int st, int nc, 
       for (int pr = 0; pr < TW / 2; ++pr) {
         const uint2 lo = __builtin_bit_cast(uint2, res[2 * pr][i]);
         const uint2 hi = __builtin_bit_cast(uint2, res[2 * pr + 1][i]);
-        const uint2 send = odd ? lo : hi;
-        uint2 recv;
-        recv.x = __shfl_xor((int)send.x, 16);
-        recv.y = __shfl_xor((int)send.y, 16);
-        // even g: own tile 2pr columns 4g .. 4g + 3, then the partner's
-        // 4g + 4 .. 4g + 7; odd g: the partner's tile 2pr + 1 columns
-        // 4g - 4 .. 4g - 1, then its own 4g .. 4g + 3
-        const uint4 v = odd ? uint4{recv.x, recv.y, hi.x, hi.y} : uint4{lo.x, lo.y, recv.x, recv.y};
+        // gfx950's row swap exchanges the odd 16-lane rows of its first
+        // operand with the even rows of its second (a VALU op; a shuffle
+        // through LDS cost a wait per store): afterwards an even-g lane
+        // holds its own tile 2pr columns 4g .. 4g + 3, then the partner's
+        // 4g + 4 .. 4g + 7, and an odd-g lane the partner's tile 2pr + 1
+        // columns 4g - 4 .. 4g - 1, then its own 4g .. 4g + 3
+        const auto sx = __builtin_amdgcn_permlane16_swap(lo.x, hi.x, false, false);
+        const auto sy = __builtin_amdgcn_permlane16_swap(lo.y, hi.y, false, false);
+        const uint4 v = uint4{sx[0], sy[0], sx[1], sy[1]};
         const int col = 16 * (jg0 + 2 * pr + (odd ? 1 : 0)) + 4 * (g & 2);
         if (t < rows)
           *reinterpret_cast<uint4 *>((T *)a.out + ((tok0 + t) * a.H + h) * D + col) = v;
