@@ -526,6 +526,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
     T *tf = (T *)a.Wf + ch * (int64_t)(64 * 64) + (int64_t)w * KS_C * 64 * 8;
 #pragma unroll
     for (int kt = 0; kt < KS_C; ++kt) {
+      // rows 0 .. 31 have no columns 32 .. 63 (T is lower triangular): those
+      // two fragments are neither stored here nor read by the state pass
+      if (kt > 0 && w < 2) continue;
       float y[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -840,6 +843,7 @@ intra_tform_shared_kernel(Args a) {
       T *tf = (T *)a.Wf + ch * (int64_t)(64 * 64) + (int64_t)w * KS_C * 64 * 8;
 #pragma unroll
       for (int kt = 0; kt < KS_C; ++kt) {
+        if (kt > 0 && w < 2) continue;  // above the diagonal: zero, not stored
         float y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {

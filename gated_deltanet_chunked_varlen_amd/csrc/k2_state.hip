@@ -250,8 +250,14 @@ struct TSlotGeo {
   static constexpr int G_OFF = T_OFF + T_BYTES;
   static constexpr int R_OFF = G_OFF + 256;       // two rows of 64 floats
   static constexpr int BYTES = R_OFF + 512;
-  static constexpr int NK = K_BYTES / 1024, NV = V_BYTES / 1024, NTF = T_BYTES / 1024;
+  static constexpr int NK = K_BYTES / 1024, NV = V_BYTES / 1024;
+  // the factor's fragments (it, kt) = (0, 1) and (1, 1), rows 0 .. 31 and
+  // columns 32 .. 63, lie above the diagonal of a lower-triangular matrix:
+  // they are zero, and neither stored nor loaded nor multiplied
+  static constexpr int NTF = 6;
   static constexpr int NP = NK + NV + NTF + 3;    // loads per chunk (three 256-byte rows)
+  // fragment index (it * 2 + kt) of the j-th loaded factor fragment
+  __device__ __forceinline__ static int tfrag(int j) { return j < 2 ? 2 * j : j + 2; }
 
   // v row r's unit permutation: rows that share banks (256 / VROW of them
   // apart) get different units
@@ -296,7 +302,8 @@ struct TLoader {
         const int r = (1024 / SG::VROW) * (i - SG::NK) + lane / SG::VU, p = lane % SG::VU;
         dma16(vc + (int64_t)min(r, rows - 1) * vstride + 8 * (p ^ SG::vswz(r)), slot + i * 1024);
       } else if (i < SG::NK + SG::NV + SG::NTF) {
-        dma16(tf + (i - SG::NK - SG::NV) * 1024 + 16 * lane, slot + i * 1024);
+        const int f = SG::tfrag(i - SG::NK - SG::NV);
+        dma16(tf + f * 1024 + 16 * lane, slot + SG::T_OFF + f * 1024);
       } else if (i == SG::NK + SG::NV + SG::NTF) {
         dma4(a.Gw + ch * kChunk + lane, slot + SG::G_OFF);
       } else if (i < SG::NP) {
@@ -368,7 +375,7 @@ __device__ __forceinline__ void tform_step(const unsigned char *slot, int ct,
 #pragma unroll
   for (int kt = 0; kt < KS_C; ++kt)
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+    for (int it = kt > 0 ? 2 : 0; it < 4; ++it)  // (0, 1) and (1, 1) are zero
       tf[it][kt] = *reinterpret_cast<const frag *>(slot + SG::T_OFF +
                                                    ((it * KS_C + kt) * 64 + lane) * 16);
   // rows 16 it + 4 g .. + 3 of exp(G) / n and exp(G_last - G) / n; G_last
@@ -382,10 +389,11 @@ __device__ __forceinline__ void tform_step(const unsigned char *slot, int ct,
   const float glast = reinterpret_cast<const float *>(slot + SG::G_OFF)[kChunk - 1];
   if constexpr (early) {
 #pragma unroll
-    for (int i = 0; i < 4 * KS_C; ++i) {
+    for (int i = 0; i < 7; ++i) {    // 16 products, 15 LDS reads
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two products
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -409,7 +417,7 @@ __device__ __forceinline__ void tform_step(const unsigned char *slot, int ct,
 #pragma unroll
   for (int kt = 0; kt < KS_C; ++kt)
 #pragma unroll
-    for (int it = 0; it < 4; ++it) acc[it] = M::mma(tf[it][kt], yt[kt], acc[it]);
+    for (int it = kt > 0 ? 2 : 0; it < 4; ++it) acc[it] = M::mma(tf[it][kt], yt[kt], acc[it]);
   frag kc[NT][KS_C];
 #pragma unroll
   for (int it = 0; it < NT; ++it)
@@ -421,10 +429,11 @@ __device__ __forceinline__ void tform_step(const unsigned char *slot, int ct,
     }
   if constexpr (early) {
 #pragma unroll
-    for (int i = 0; i < 4 * KS_C; ++i) {
+    for (int i = 0; i < 6; ++i) {    // 6 products, 32 LDS reads
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // four LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);  // five LDS reads
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   float accf[16];

@@ -148,7 +148,9 @@ def tform_workspace_offsets(T, N, H, D, hq, hk):
 
 def _decode_factor(block):
     """[64, 64] from the operand-fragment order: fragment (w, kt), lane
-    16 g + c, slot e holds row 16 w + c, column 32 kt + 16 (e / 4) + 4 g + e % 4."""
+    16 g + c, slot e holds row 16 w + c, column 32 kt + 16 (e / 4) + 4 g + e % 4.
+    Fragments (0, 1) and (1, 1) lie above the diagonal and are not stored:
+    the workspace handed in is zeroed, so they decode as the zeros they are."""
     out = np.zeros((64, 64))
     b = block.reshape(4, 2, 64, 8)
     for w in range(4):
