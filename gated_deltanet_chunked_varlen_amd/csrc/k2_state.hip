@@ -535,10 +535,12 @@ __device__ __forceinline__ void output_regs(const Args &a, const OutRegs<T, D> &
     }
     // acc[e] = O[t][16 jv + 4g + e]
     if (t < rows) {
-      typename M::half o4;
+      f32x4 sc;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (T)(a.scale * acc[e]);
-      *reinterpret_cast<typename M::half *>(out + ((tok0 + t) * H + h) * D + 16 * jv + 4 * g) = o4;
+      for (int e = 0; e < 4; ++e) sc[e] = a.scale * acc[e];
+      // one vector conversion: two packed converts, no repacking
+      *reinterpret_cast<typename M::half *>(out + ((tok0 + t) * H + h) * D + 16 * jv + 4 * g) =
+          __builtin_convertvector(sc, typename M::half);
     }
   }
 }
@@ -571,8 +573,10 @@ __device__ __forceinline__ void output_values(const Args &a, const OutRegs<T, D>
 #pragma unroll
       for (int kt = 0; kt < KS_C; ++kt) acc = M::mma(nf[kt], r.p1[kt], acc);
     }
+    f32x4 sc;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) res[i][e] = (T)(a.scale * acc[e]);
+    for (int e = 0; e < 4; ++e) sc[e] = a.scale * acc[e];
+    res[i] = __builtin_convertvector(sc, typename M::half);  // two packed converts
   }
 }
 
