@@ -241,13 +241,35 @@ template <typename T, int D> struct Geo {
 // increasing x within a lane, then (p0 + p1) + (p2 + p3).  Every kernel that
 // normalises q or k uses this, so all of them see bit-identical rows.
 // ---------------------------------------------------------------------------
+// Lane moves through the VALU's data-parallel-primitive (DPP) controls of
+// gfx9 instead of a shuffle through LDS: CTRL is the control word, rows (16
+// lanes) outside ROW_MASK and lanes whose source falls outside their row read
+// 0.  Controls used: quad_perm [1,0,3,2] = 0xB1 and [2,3,0,1] = 0x4E,
+// row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: steps of 1, 2, 4, 8
+// within each row, then each row's total carried into the later rows.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x += dpp_or_zero<0x111>(x);
+  x += dpp_or_zero<0x112>(x);
+  x += dpp_or_zero<0x114>(x);
+  x += dpp_or_zero<0x118>(x);
+  x += dpp_or_zero<0x142, 0xA>(x);  // lane 15 of rows 0, 2 into rows 1, 3
+  x += dpp_or_zero<0x143, 0xC>(x);  // lane 31 into rows 2, 3
+  return x;
+}
+
 template <int D>
 __device__ __forceinline__ float row_inv_norm(const float (&x)[D / 4]) {
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < D / 4; ++i) s = fmaf(x[i], x[i], s);
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
+  s += dpp_or_zero<0xB1>(s);  // lane parts p ^ 1
+  s += dpp_or_zero<0x4E>(s);  // lane parts p ^ 2
   return 1.0f / sqrtf(s + kNormEps);
 }
 

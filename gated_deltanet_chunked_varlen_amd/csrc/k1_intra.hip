@@ -96,11 +96,7 @@ __global__ void __launch_bounds__(256) intra_kernel(Args a) {
       la = a.g ? logf(a.g[gi]) : 0.f;
       be = a.beta ? a.beta[gi] : 1.f;
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float y = __shfl_up(la, o);
-      if (lane >= o) la += y;
-    }
+    la = wave_prefix_sum(la);
     AT[t][64] = la;
     AT[t][65] = be;
     a.Gw[ch * kChunk + t] = la;
@@ -373,11 +369,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
       la = a.g ? logf(a.g[gi]) : 0.f;
       be = a.beta ? a.beta[gi] : 1.f;
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float y = __shfl_up(la, o);
-      if (lane >= o) la += y;
-    }
+    la = wave_prefix_sum(la);
     AT[t][64] = la;
     AT[t][65] = be;
     a.Gw[ch * kChunk + t] = la;
@@ -709,11 +701,7 @@ intra_tform_shared_kernel(Args a) {
       la = a.g ? logf(a.g[gi]) : 0.f;
       be = a.beta ? a.beta[gi] : 1.f;
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float y = __shfl_up(la, o);
-      if (lane >= o) la += y;
-    }
+    la = wave_prefix_sum(la);
     sm.G[wave][t] = la;
     sm.B[wave][t] = be;
     a.Gw[ws_index(f, h, a.cap) * kChunk + t] = la;
