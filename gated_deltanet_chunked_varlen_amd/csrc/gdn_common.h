@@ -251,6 +251,32 @@ __device__ __forceinline__ float dpp_or_zero(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
 }
 
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_or_zero_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix sum and prefix maximum of non-negative ints over the 64
+// lanes of a wave (exact; 0 is the identity of both)
+__device__ __forceinline__ int wave_prefix_sum_i(int x) {
+  x += dpp_or_zero_i<0x111>(x);
+  x += dpp_or_zero_i<0x112>(x);
+  x += dpp_or_zero_i<0x114>(x);
+  x += dpp_or_zero_i<0x118>(x);
+  x += dpp_or_zero_i<0x142, 0xA>(x);
+  x += dpp_or_zero_i<0x143, 0xC>(x);
+  return x;
+}
+__device__ __forceinline__ int wave_prefix_max_nonneg(int x) {
+  x = max(x, dpp_or_zero_i<0x111>(x));
+  x = max(x, dpp_or_zero_i<0x112>(x));
+  x = max(x, dpp_or_zero_i<0x114>(x));
+  x = max(x, dpp_or_zero_i<0x118>(x));
+  x = max(x, dpp_or_zero_i<0x142, 0xA>(x));
+  x = max(x, dpp_or_zero_i<0x143, 0xC>(x));
+  return x;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave: steps of 1, 2, 4, 8
 // within each row, then each row's total carried into the later rows.
 __device__ __forceinline__ float wave_prefix_sum(float x) {
@@ -356,22 +382,13 @@ __device__ __forceinline__ SeqLane seq_lane(const void *cu, int cu_type, int N, 
     s.raw = cu ? load_index_any(cu, cu_type, lane) : (lane == 0 ? 0 : T);
     x = s.raw < 0 ? 0 : (s.raw > T ? T : s.raw);
   }
-  int bos = (int)x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(bos, o);
-    if (lane >= o) bos = bos > y ? bos : y;
-  }
+  // running maximum and chunk counts by DPP lane moves (no LDS round trips)
+  const int bos = wave_prefix_max_nonneg((int)x);
   const int nxt = __shfl_down(bos, 1);
   s.bos = bos;
   s.len = lane < N ? nxt - bos : 0;
   const int nch = (s.len + kChunk - 1) / kChunk;
-  int cc = nch;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(cc, o);
-    if (lane >= o) cc += y;
-  }
+  const int cc = wave_prefix_sum_i(nch);
   s.cc1 = cc;
   s.cc0 = cc - nch;
   return s;
