@@ -314,6 +314,55 @@ struct TLoader {
   }
 };
 
+// L2 warm-up of a T-form chunk (one tile per workgroup, intermediates in
+// HBM): the NWG workgroups of a (sequence, head) split the 128-byte lines
+// every one of them reads -- the chunk's k and v rows (whole rows; rows past
+// the chunk's end clamp to its last row, as the loaders do), the factor
+// block, the q and P blocks and the three rows -- and touch each once, a
+// 4-byte direct load per line into a scratch LDS word, so that the loaders'
+// requests a chunk or two later find the lines in L2.
+template <typename T, int D, int TW>
+struct TWarm {
+  static constexpr int NWG = D / 16 / TW;
+  static constexpr int LINE = 128, ROWL = D * (int)sizeof(T) / LINE;  // lines per k / v row
+  static constexpr int KL = 64 * ROWL, TL = 64 * 64 * (int)sizeof(T) / LINE;
+  static constexpr int QL = 64 * D * (int)sizeof(T) / LINE;
+  static constexpr int ALL = 2 * KL + TL + QL + TL + 6;  // k, v, factor, q, P, gate and scale rows
+  __device__ __forceinline__ static void touch(const Args &a, int64_t ch, int cc, int h, int jw,
+                                               int lane, int len, const T *k, const T *v,
+                                               int64_t kstride, int64_t vstride,
+                                               unsigned char *junk) {
+    const int rows = min(kChunk, len - kChunk * cc);
+    const unsigned char *kc = (const unsigned char *)(k + (int64_t)kChunk * cc * kstride);
+    const unsigned char *vc = (const unsigned char *)(v + (int64_t)kChunk * cc * vstride);
+    const unsigned char *tf = (const unsigned char *)a.Wf + ch * (TL * LINE);
+    const unsigned char *qf = (const unsigned char *)a.Qf + q_block(a, ch, h) * (QL * LINE);
+    const unsigned char *pf = (const unsigned char *)a.Pf + ch * (TL * LINE);
+#pragma unroll
+    for (int l0 = 0; l0 < ALL; l0 += NWG * 64) {
+      const int l = min(l0 + jw + NWG * lane, ALL - 1);
+      const unsigned char *src;
+      if (l < 2 * KL) {
+        const int m = l < KL ? l : l - KL;
+        const int r = min(m / ROWL, rows - 1), part = m % ROWL;
+        src = l < KL ? kc + (int64_t)r * kstride * (int64_t)sizeof(T) + part * LINE
+                     : vc + (int64_t)r * vstride * (int64_t)sizeof(T) + part * LINE;
+      } else if (l < 2 * KL + TL) {
+        src = tf + (l - 2 * KL) * LINE;
+      } else if (l < 2 * KL + TL + QL) {
+        src = qf + (l - 2 * KL - TL) * LINE;
+      } else if (l < 2 * KL + 2 * TL + QL) {
+        src = pf + (l - 2 * KL - TL - QL) * LINE;
+      } else {
+        const int e = l - 2 * KL - 2 * TL - QL;   // 0, 1: gate row; 2 .. 5: scale rows
+        src = e < 2 ? (const unsigned char *)(a.Gw + ch * kChunk) + e * LINE
+                    : (const unsigned char *)(a.Bw + ch * 128) + (e - 2) * LINE;
+      }
+      dma4(src, junk);
+    }
+  }
+};
+
 // One chunk of the recurrence in the T form for compute wave ct's 16-column
 // tile (as chunk_step, with the operands of a T-form slot).  The chunk-start
 // state and N (unscaled) go to the output waves through xb.
@@ -692,8 +741,11 @@ template <> struct FusedRoles<4> {
 // end exit at once (segment 0 still runs for an empty sequence, whose final
 // state is its initial state).
 //
-// TF: the T form (four tiles, no context parallelism; see TSlotGeo).  Its
-// slots hold the v rows too, so the compute waves fetch no U.
+// TF: the T form (no context parallelism; see TSlotGeo).  Its slots hold the
+// v rows too, so the compute waves fetch no U.  With one tile per workgroup
+// and the intermediates in HBM its warm-up wave touches the chunk's lines two
+// chunks ahead (TWarm; 262 144 tokens x 32 heads: state pass 4.64 -> 3.94 ms,
+// the same at three chunks ahead, 4.83 ms at one).
 template <typename T, int D, int TW, bool CP = false, bool SHK = false, bool TF = false>
 __global__ void __launch_bounds__(64 * FusedRoles<TW>::kWaves)
 state_output_kernel(Args a) {
@@ -859,13 +911,23 @@ state_output_kernel(Args a) {
       ++st;
     }
     if (st < nc + 2) output_wave_step<T, D, TW>(a, st, nc, len, sbos, ch0, jg0, h, lane, ow, r0, r1, xbuf);
-  } else if (!TF && wave == R::warm_wave(hbm)) {
+  } else if ((!TF || TW == 1) && wave == R::warm_wave(hbm)) {
     // ---------------- L2 warm-up wave ---------------------------------------
     const int ahead = a.warm;
-    for (int cc = 0; cc < ahead && cc < nc; ++cc) L2Warm<T, D, TW>::touch(a, ch0 + cc, h, jw, lane, junk);
+    const int kh = h / (H / a.hk), vh = h / (H / a.hv);
+    const T *kb = (const T *)a.k + ((int64_t)sbos * a.hk + kh) * D;
+    const T *vb = (const T *)a.v + ((int64_t)sbos * a.hv + vh) * D;
+    auto touch = [&](int cc) {
+      if constexpr (TF)
+        TWarm<T, D, TW>::touch(a, ch0 + cc, cc, h, jw, lane, len, kb, vb, (int64_t)a.hk * D,
+                               (int64_t)a.hv * D, junk);
+      else
+        L2Warm<T, D, TW>::touch(a, ch0 + cc, h, jw, lane, junk);
+    };
+    for (int cc = 0; cc < ahead && cc < nc; ++cc) touch(cc);
     for (int st = 0; st <= nc + 1; ++st) {
       __builtin_amdgcn_s_barrier();
-      if (ahead > 0 && st + ahead < nc) L2Warm<T, D, TW>::touch(a, ch0 + (int64_t)(st + ahead), h, jw, lane, junk);
+      if (ahead > 0 && st + ahead < nc) touch(st + ahead);
     }
     wait_vm<0>();
   } else if (part >= 0) {
