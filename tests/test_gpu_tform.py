@@ -122,6 +122,20 @@ def test_tform_one_tile_pass_large_call():
     _check(wl, gpu, tl.run_oracle(wl))
 
 
+def test_tform_one_tile_pass_ragged_sequences_with_warmup():
+    # two sequences of 39 963 and 25 541 tokens (ragged last chunks), four
+    # heads: one tile per workgroup with the intermediates past the
+    # last-level cache, so the L2 warm-up wave runs, clamping the rows of
+    # each sequence's last chunk like the loaders
+    wl = W.make(71, [39963, 25541], 4, 4, 4, 128, "bf16", l2norm_in_kernel=True,
+                init="seq", init_std=0.3, checkpoint_every=4096,
+                name="tform_one_tile_ragged")
+    assert _tiles_per_cu(wl) <= 1
+    gpu = tl.run_gpu(wl, status=True, use_cp=False)
+    assert gpu["status"] == 0
+    _check(wl, gpu, tl.run_oracle(wl))
+
+
 def _align(x):
     return (x + 255) // 256 * 256
 
