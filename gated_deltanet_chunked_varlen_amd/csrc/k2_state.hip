@@ -549,51 +549,6 @@ struct OutRegs {
   }
 };
 
-// The output of one chunk for one 16-column tile (output wave ow).
-template <typename T, int D>
-__device__ __forceinline__ void output_regs(const Args &a, const OutRegs<T, D> &r,
-                                            const typename Mfma<T>::frag *xb, int jv,
-                                            int64_t tok0, int rows, int h, int lane, int ow) {
-  using M = Mfma<T>;
-  typedef typename M::frag frag;
-  constexpr int KS_D = Geo<T, D>::KS_D, KS_C = Geo<T, D>::KS_C;
-  const int g = lane >> 4, c = lane & 15;
-  frag sf[KS_D], nf[KS_C];
-#pragma unroll
-  for (int kt = 0; kt < KS_D; ++kt) sf[kt] = xb[kt * 64 + lane];
-#pragma unroll
-  for (int kt = 0; kt < KS_C; ++kt) nf[kt] = xb[(KS_D + kt) * 64 + lane];
-  T *out = (T *)a.out;
-  const int H = a.H;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int tt = i == 0 ? ow : 3 - ow;
-    const int t = 16 * tt + c;  // this lane's output row
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kt = 0; kt < KS_D; ++kt) acc = M::mma(sf[kt], r.q[i][kt], acc);
-    const float gam = gexp(r.g[i]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] *= gam;
-    // token tile 0 or 1 sees only the first k-step of P; 2 or 3 both
-    if (i == 0) {
-      acc = M::mma(nf[0], r.p0, acc);
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < KS_C; ++kt) acc = M::mma(nf[kt], r.p1[kt], acc);
-    }
-    // acc[e] = O[t][16 jv + 4g + e]
-    if (t < rows) {
-      f32x4 sc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sc[e] = a.scale * acc[e];
-      // one vector conversion: two packed converts, no repacking
-      *reinterpret_cast<typename M::half *>(out + ((tok0 + t) * H + h) * D + 16 * jv + 4 * g) =
-          __builtin_convertvector(sc, typename M::half);
-    }
-  }
-}
-
 // The output values of one chunk for one 16-column tile (output wave ow),
 // scaled and rounded, without storing them: res[i] for token tile i.
 template <typename T, int D>
@@ -679,9 +634,22 @@ __device__ __forceinline__ void output_wave_step(const Args &a, int st, int nc, 
       }
     }
   } else {
-#pragma unroll
-    for (int t = 0; t < TW; ++t)
-      output_regs<T, D>(a, proc, xbuf[t][oc & 1], jg0 + t, tok0, rows, h, lane, ow);
+    // one tile: the same row swap pairs the wave's two token tiles instead,
+    // so that every lane stores 16 contiguous bytes: an even-g lane columns
+    // 4g .. 4g + 7 of its row in token tile ow, an odd-g lane columns
+    // 4g - 4 .. 4g + 3 of its row in token tile 3 - ow
+    typename Mfma<T>::half res[2];
+    output_values<T, D>(a, proc, xbuf[0][oc & 1], lane, ow, res);
+    const int g = lane >> 4, c = lane & 15;
+    const bool odd = (g & 1) != 0;
+    const uint2 lo = __builtin_bit_cast(uint2, res[0]);
+    const uint2 hi = __builtin_bit_cast(uint2, res[1]);
+    const auto sx = __builtin_amdgcn_permlane16_swap(lo.x, hi.x, false, false);
+    const auto sy = __builtin_amdgcn_permlane16_swap(lo.y, hi.y, false, false);
+    const uint4 v = uint4{sx[0], sy[0], sx[1], sy[1]};
+    const int t = 16 * (odd ? 3 - ow : ow) + c;
+    const int col = 16 * jg0 + 4 * (g & 2);
+    if (t < rows) *reinterpret_cast<uint4 *>((T *)a.out + ((tok0 + t) * a.H + h) * D + col) = v;
   }
 }
 
